@@ -1,0 +1,179 @@
+/*
+ * rlk_logp.h -- deterministic selected-token log-probability over a
+ * tile-decomposed vocabulary, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages, cited by title and section):
+ *
+ *   [PR289] PR #289 "[WS2][PR4][Logp] feat: add distributed TP/CP logprob drift
+ *           report": the stacked PR1 commit messages define the contract --
+ *           padded vs real vocabulary, an explicit active mask plus
+ *           ignore_index, padded columns masked to -inf before per-tile fp32
+ *           (max, sumexp) partials, a (-inf, 0) identity partial for
+ *           padding-only or all -inf tiles, a merge in fixed global tile order,
+ *           and fp32 selected-logprob and fp32 LSE outputs.  The review excerpt
+ *           of the op's apply() shows the target-range check on active tokens
+ *           and the "non-finite logsumexp on an active row" error.
+ *   [I323]  Issue #323 "[WS2][Logprob] H100 validation and reproduction guide
+ *           for Issue #241 PR1-PR5", "Test Order / 2. Six-Case TP/CP Matrix":
+ *           64 vocabulary tiles over a real = padded vocabulary of 151936;
+ *           "4. Cross-Topology Bitwise Check": regrouping the tiles across
+ *           1/2/4 vocabulary shards leaves the fp32 outputs bitwise identical.
+ *
+ * For row r of the logits X (bf16, [N, ld]) with real vocabulary V_real:
+ *
+ *   LSE_r  = log sum_{j < V_real} exp(X[r, j])
+ *   a_r    = (mask == NULL || mask[r] != 0) && target[r] != ignore_index
+ *   logp_r = a_r ? float(X[r, target[r]]) - LSE_r : +0.0f
+ *   dX[r, j] = a_r ? g_r * ([j == target[r]] - exp(X[r, j] - LSE_r)) : +0   (j < V_real)
+ *   dX[r, j] = +0                                                   (V_real <= j < V_pad)
+ *
+ * The forward computes it as the pages do: tile t covers the columns
+ * [floor(t*V_pad/T), floor((t+1)*V_pad/T)); each tile yields an fp32
+ * (max, sumexp) over its real columns (columns >= V_real never contribute and
+ * are never read for arithmetic, so any bit pattern may sit there); the T
+ * partials are merged in ascending tile order into LSE.  Tiles may be grouped
+ * into S contiguous "virtual shards" (shard s = tiles [floor(s*T/S),
+ * floor((s+1)*T/S)), one launch each, standing in for the pages' tensor-
+ * parallel ranks); every tile's arithmetic is independent of the launch that
+ * computes it, so logp and LSE are bitwise identical for every S, across
+ * repeated calls, and for a row whatever other rows share the call.
+ *
+ * Conventions shared by every call:
+ *   - Ownership: the caller allocates and owns every buffer, device and host,
+ *     including the workspace.  The library never allocates, frees or keeps a
+ *     pointer after a call returns.  Its only global state is the per-thread
+ *     error-detail string.
+ *   - Pointers marked (device) must be device-accessible memory of the device
+ *     that is current on the calling thread; `desc` is a host pointer.
+ *   - Streams: every call enqueues its kernels on `stream` (0 = the null
+ *     stream) and returns without waiting, unless RLK_FLAG_VALIDATE is set.
+ *   - Host errors (null pointer, shape, tiling, alignment, workspace, dtype)
+ *     are detected before anything is enqueued; nothing is written then.
+ *   - Data errors (an effective-active target outside [0, V_real); a
+ *     non-finite LSE on an effective-active row) are found on the device.  The
+ *     outputs are always safe: a bad target yields NaN and no out-of-bounds
+ *     read.  With RLK_FLAG_VALIDATE the call synchronises the stream and
+ *     reports them as RLK_ERR_TARGET_RANGE / RLK_ERR_NONFINITE_LSE.
+ *   - There is one code path and no fallback: if the GPU path cannot run, the
+ *     call fails.
+ */
+#ifndef RLK_LOGP_H_
+#define RLK_LOGP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rlk_status {
+  RLK_OK = 0,
+  RLK_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                        */
+  RLK_ERR_BAD_SHAPE = 2,     /* sizes violate the limits stated on rlk_logp_desc  */
+  RLK_ERR_BAD_TILING = 3,    /* T or S outside their ranges                        */
+  RLK_ERR_ALIGNMENT = 4,     /* a pointer or leading dimension is misaligned       */
+  RLK_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required            */
+  RLK_ERR_DTYPE = 6,         /* unknown rlk_dtype                                  */
+  RLK_ERR_TARGET_RANGE = 7,  /* (VALIDATE) an effective-active target not in [0, V_real) */
+  RLK_ERR_NONFINITE_LSE = 8, /* (VALIDATE) non-finite LSE on an effective-active row */
+  RLK_ERR_HIP = 9            /* the HIP runtime reported an error                   */
+} rlk_status;
+
+typedef enum rlk_dtype { RLK_DTYPE_F32 = 0, RLK_DTYPE_BF16 = 1 } rlk_dtype;
+
+/* Synchronise `stream` after the launches and turn the device status words
+ * into RLK_ERR_TARGET_RANGE (checked first) or RLK_ERR_NONFINITE_LSE. */
+#define RLK_FLAG_VALIDATE 1u
+
+/* Problem description (host struct, read during the call only).
+ * Limits (else RLK_ERR_BAD_SHAPE / RLK_ERR_BAD_TILING):
+ *   num_tokens N        >= 0 (N == 0 enqueues nothing and returns RLK_OK)
+ *   real_vocab V_real   >= 1 and <= padded_vocab
+ *   padded_vocab V_pad  <= 2^31 - 1 (targets are int32 column indices)
+ *   ld_logits           >= V_pad, a multiple of 8 elements (16-byte rows)
+ *   num_vocab_tiles T   in [1, V_pad]; the pages fix T = 64
+ *   num_virtual_shards S in [1, T]; it must not and does not change results
+ *   ignore_index        any int32; the usual value is -100
+ *   flags               0 or RLK_FLAG_VALIDATE                                  */
+typedef struct rlk_logp_desc {
+  int64_t num_tokens;
+  int64_t real_vocab;
+  int64_t padded_vocab;
+  int64_t ld_logits;
+  int32_t num_vocab_tiles;
+  int32_t num_virtual_shards;
+  int32_t ignore_index;
+  uint32_t flags;
+} rlk_logp_desc;
+
+/* Bytes of device workspace that rlk_logp_fwd and rlk_logp_bwd need for
+ * `desc` (0 if `desc` is NULL or invalid).  Layout, from the workspace base
+ * (which must be 256-byte aligned):
+ *   [0, 256)                     uint32 status words: [0] target-range flag,
+ *                                [1] non-finite-LSE flag (nonzero = seen)
+ *   [256, 256 + P)               float pmax[N][T]  per-tile maxima
+ *   [256 + P, 256 + 2P)          float psum[N][T]  per-tile sums of exp(x - pmax)
+ * where P = N*T*4 rounded up to a multiple of 256.  After rlk_logp_fwd the
+ * partials hold the per-tile statistics of [PR289]'s contract (the identity
+ * partial is (-inf, 0)); they stay valid until the workspace is reused. */
+size_t rlk_logp_workspace_bytes(const rlk_logp_desc* desc);
+
+/* Forward: per-tile partials, fixed-order merge, target gather.
+ *   logits      (device) bf16 [N, ld_logits], 16-byte aligned; columns
+ *               [V_real, ld_logits) are never used in arithmetic.
+ *   targets     (device) int32 [N]; read only where the mask is set.
+ *   active_mask (device) uint8 [N], nonzero = active; NULL = all active.
+ *   logp        (device) float [N] out: selected log-probability; +0.0 on
+ *               rows that are not effective-active; NaN for a bad target.
+ *   lse         (device) float [N] out: LSE over the real vocabulary for every
+ *               row (-inf for a row whose real logits are all -inf; NaN if one
+ *               is NaN or +inf).
+ *   workspace   (device) >= rlk_logp_workspace_bytes(desc) bytes, 256-byte
+ *               aligned.
+ * Rows are independent; outputs for row r depend only on row r's inputs. */
+rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, float* logp, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Backward: dX = g * (onehot(target) - softmax(X)) on effective-active rows,
+ * using the forward's LSE ([PR289]: the op is an autograd function whose
+ * gradient flows to the logits; the formula is the derivative of logp_r).
+ *   logits, targets, active_mask  as for rlk_logp_fwd (inactive rows' logits
+ *               are not read).
+ *   lse         (device) float [N]: the forward's LSE output.
+ *   grad_logp   (device) float [N]: upstream gradient g; read on
+ *               effective-active rows only.
+ *   dlogits     (device) [N, ld_dlogits] of `dlogits_dtype`, 16-byte aligned,
+ *               out.  Every element of columns [0, V_pad) is written: +0 on
+ *               inactive rows and padded columns; on a row with a bad target
+ *               the real columns are NaN.  Columns [V_pad, ld_dlogits) are not
+ *               touched.  bf16 results are rounded to nearest even.
+ *   ld_dlogits  >= V_pad, a multiple of 8 elements.
+ *   workspace   as for rlk_logp_fwd (only the status words are used).
+ * With RLK_FLAG_VALIDATE a bad effective-active target reports
+ * RLK_ERR_TARGET_RANGE. */
+rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, const float* lse, const float* grad_logp,
+                        void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only geometry (no device access): writes T+1 tile bounds
+ * floor(t*V_pad/T) to `bounds` and S+1 shard starts floor(s*T/S) to
+ * `shard_first_tile` (either may be NULL).  Same limits as the descriptor. */
+rlk_status rlk_logp_tile_geometry(int64_t padded_vocab, int32_t num_vocab_tiles,
+                                  int32_t num_virtual_shards, int64_t* bounds,
+                                  int32_t* shard_first_tile);
+
+/* Static name of a status code. */
+const char* rlk_status_string(rlk_status status);
+
+/* Reason text for the last non-OK status returned on the calling thread
+ * ("" if none).  Valid until the next call on that thread. */
+const char* rlk_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_LOGP_H_ */

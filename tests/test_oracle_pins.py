@@ -1,0 +1,356 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is trusted only because of these checks, none of which re-uses its
+arithmetic: exact bf16 bit patterns, integer invariants of the tile geometry,
+a pure-Python brute force on tiny vocabularies (tests/brute.py), closed forms,
+finite differences, and float64 library routines (torch.logsumexp,
+log_softmax, cross_entropy, autograd).  ``test_pins_catch_planted_mistakes``
+builds deliberately broken copies of the oracle and checks that the pins fail.
+"""
+from __future__ import annotations
+
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import brute
+
+IGNORE = -100
+LN_151936 = math.log(151936)
+
+
+# --------------------------------------------------------------------------
+# helpers (input construction only; no method arithmetic)
+# --------------------------------------------------------------------------
+def bf16_bits(values) -> np.ndarray:
+    """Round float values to bf16 (torch RNE) and return the bit patterns."""
+    t = torch.as_tensor(np.asarray(values, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def random_bf16(rng: np.random.Generator, shape, sigma=2.0) -> np.ndarray:
+    return bf16_bits(rng.normal(0.0, sigma, size=shape))
+
+
+def decode(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64 via struct (brute path), elementwise."""
+    flat = [brute.bf16_bits_to_float(b) for b in bits.reshape(-1)]
+    return np.asarray(flat, dtype=np.float64).reshape(bits.shape)
+
+
+def close(a, b, tol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    with np.errstate(invalid="ignore"):
+        both_nan = np.isnan(a) & np.isnan(b)
+        same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+        diff = np.abs(a - b)
+        ok = both_nan | same_inf | (diff <= tol)
+        assert ok.all(), f"max diff {diff[~ok].max()} > {tol}"
+
+
+# --------------------------------------------------------------------------
+# pins, each a function of an oracle instance
+# --------------------------------------------------------------------------
+def pin_bf16_decode(o):
+    known = {0x3F80: 1.0, 0xBF80: -1.0, 0x4049: 3.140625, 0x0000: 0.0, 0x4000: 2.0,
+             0x7F80: math.inf, 0xFF80: -math.inf, 0x0001: 2.0 ** -133,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0xC2C8: -100.0}
+    for bits, val in known.items():
+        assert o.bf16_to_f64(bits) == val, hex(bits)
+    assert math.copysign(1.0, o.bf16_to_f64(0x8000)) == -1.0
+    assert math.isnan(o.bf16_to_f64(0x7FC0))
+    # every pattern against torch's bfloat16 -> float64 conversion
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = np.array([o.bf16_to_f64(int(b)) for b in range(0, 65536, 7)])
+    sel = ref[::7]
+    assert np.array_equal(np.isnan(got), np.isnan(sel))
+    m = ~np.isnan(sel)
+    assert np.array_equal(got[m], sel[m])
+
+
+def pin_geometry(o):
+    # the pages' sizes: 64 tiles over 151936 and 152576 columns
+    assert set(np.diff(o.tile_bounds(151936, 64))) == {2374}
+    assert set(np.diff(o.tile_bounds(152576, 64))) == {2384}
+    rng = np.random.default_rng(5)
+    cases = [(10, 3), (7, 7), (1, 1), (100, 8), (152576, 63), (151936, 1)]
+    cases += [(int(v), int(rng.integers(1, v + 1))) for v in rng.integers(1, 5000, size=40)]
+    for v, t in cases:
+        b = o.tile_bounds(v, t)
+        assert b.shape == (t + 1,)
+        assert b[0] == 0 and b[-1] == v  # exact cover, last bound pinned to V
+        w = np.diff(b)
+        assert (w >= 1).all()  # T <= V: no empty tile
+        assert set(w) <= {v // t, -(-v // t)}  # equal as possible
+        assert w.sum() == v
+    for t in (64, 63, 9, 1):
+        for s in sorted({1, 2, 3, 4, 7, 8, t} & set(range(1, t + 1))):
+            f = o.shard_tiles(t, s)
+            assert f[0] == 0 and f[-1] == t
+            assert set(np.diff(f)) <= {t // s, -(-t // s)} and (np.diff(f) >= 1).all()
+    assert list(np.diff(o.shard_tiles(64, 4))) == [16] * 4
+    for bad in ((0, 1), (5, 0), (5, 6)):
+        with pytest.raises(oracle.OracleError):
+            o.tile_bounds(*bad)
+    with pytest.raises(oracle.OracleError):
+        o.shard_tiles(8, 9)
+
+
+def pin_fwd_brute(o):
+    rng = np.random.default_rng(11)
+    for v in (1, 2, 3, 5, 8, 17, 64):
+        n = 2 * v + 3
+        ld = v + 8 + (-v) % 8  # padding and an ld wider than the row
+        bits = random_bf16(rng, (n, ld))
+        tgt = np.concatenate([np.arange(v), rng.integers(0, v, size=n - v)]).astype(np.int32)
+        mask = rng.random(n) < 0.8
+        tgt[rng.random(n) < 0.15] = IGNORE
+        logp, lse, rc, _ = o.fwd(bits, tgt, mask, real_vocab=v)
+        assert rc == 0
+        rows = decode(bits[:, :v]).tolist()
+        bl, bs = brute.fwd(rows, tgt, mask, v)
+        close(logp, bl, 1e-12)
+        close(lse, bs, 1e-12)
+        # the fp64 entry point on the decoded values agrees bit for bit
+        l2, s2, _, _ = o.fwd(decode(bits), tgt, mask, real_vocab=v)
+        assert np.array_equal(l2, logp) and np.array_equal(s2, lse)
+
+
+def pin_closed_forms(o):
+    v = 151936
+    cs = np.array([0.0, 1.5, -3.0, 7.25])
+    x = np.repeat(bf16_bits(cs)[:, None], v, axis=1)
+    tgt = np.array([0, 17, v - 1, 75968], dtype=np.int32)
+    logp, lse, _, _ = o.fwd(x, tgt, None, real_vocab=v)
+    close(lse, cs + LN_151936, 1e-12)
+    close(logp, np.full(4, -LN_151936), 1e-12)
+    # one finite value a, the rest -inf: LSE == a and logp == 0, exactly
+    ninf = bf16_bits([-np.inf])[0]
+    for v2, pos, a in ((64, 5, 3.25), (151936, 151935, -7.5), (1, 0, 12.0)):
+        row = np.full((1, v2), ninf, dtype=np.uint16)
+        row[0, pos] = bf16_bits([a])[0]
+        lp, ls, _, _ = o.fwd(row, np.array([pos], np.int32), None, real_vocab=v2)
+        assert ls[0] == a and lp[0] == 0.0
+        # k equal values: a + ln k
+        k = min(v2, 9)
+        row[0, :] = ninf
+        row[0, :k] = bf16_bits([a])[0]
+        _, ls, _, _ = o.fwd(row, np.array([0], np.int32), None, real_vocab=v2)
+        close(ls, [a + math.log(k)], 1e-12)
+    # shift invariance with integer logits (exact in bf16 up to 256)
+    rng = np.random.default_rng(3)
+    ints = rng.integers(-64, 65, size=(6, 300)).astype(np.float64)
+    t6 = rng.integers(0, 300, size=6).astype(np.int32)
+    l0, s0, _, _ = o.fwd(bf16_bits(ints), t6, None, real_vocab=300)
+    l1, s1, _, _ = o.fwd(bf16_bits(ints + 64.0), t6, None, real_vocab=300)
+    close(l1, l0, 1e-12)
+    close(s1 - s0, np.full(6, 64.0), 1e-12)
+    # the selected probabilities over every target sum to one
+    for v3 in (1, 2, 5, 17):
+        row = random_bf16(rng, (1, v3))
+        rows = np.repeat(row, v3, axis=0)
+        lp, _, _, _ = o.fwd(rows, np.arange(v3, dtype=np.int32), None, real_vocab=v3)
+        assert abs(math.fsum(np.exp(lp)) - 1.0) <= 1e-12
+
+
+def pin_library(o):
+    rng = np.random.default_rng(7)
+    n, v_real, v_pad, ld = 24, 1000, 1024, 1032
+    bits = random_bf16(rng, (n, ld), sigma=3.0)
+    bits[:, v_real:] = rng.integers(0, 65536, size=(n, ld - v_real)).astype(np.uint16)
+    tgt = rng.integers(0, v_real, size=n).astype(np.int32)
+    mask = rng.random(n) < 0.7
+    tgt[3] = IGNORE
+    logp, lse, _, _ = o.fwd(bits, tgt, mask, real_vocab=v_real)
+    xt = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double()[:, :v_real]
+    close(lse, torch.logsumexp(xt, dim=1).numpy(), 1e-12)
+    act = mask & (tgt != IGNORE)
+    ls = torch.log_softmax(xt, dim=1)
+    ref = np.where(act, ls[torch.arange(n), torch.from_numpy(np.where(act, tgt, 0)).long()]
+                   .numpy(), 0.0)
+    close(logp, ref, 1e-12)
+    ce_t = torch.from_numpy(np.where(act, tgt, IGNORE)).long()
+    ce = torch.nn.functional.cross_entropy(xt, ce_t, ignore_index=IGNORE, reduction="none")
+    close(-logp, ce.numpy(), 1e-12)
+    assert np.all(logp[~act] == 0.0) and not np.signbit(logp[~act]).any()
+
+
+def pin_gradient(o):
+    rng = np.random.default_rng(13)
+    h = 1e-5
+    for v in (1, 2, 5, 17):
+        n = 5
+        x = decode(random_bf16(rng, (n, v)))
+        tgt = rng.integers(0, v, size=n).astype(np.int32)
+        mask = np.array([1, 1, 0, 1, 1], dtype=bool)
+        tgt[4] = IGNORE
+        g = rng.normal(size=n)
+        _, lse, _, _ = o.fwd(x, tgt, mask, real_vocab=v)
+        d = o.bwd(x, tgt, mask, lse, g, real_vocab=v, padded_vocab=v + 3)
+        assert d.shape == (n, v + 3) and np.all(d[:, v:] == 0.0)
+        fd = np.zeros((n, v))
+        for j in range(v):
+            xp, xm = x.copy(), x.copy()
+            xp[:, j] += h
+            xm[:, j] -= h
+            lpp, _, _, _ = o.fwd(xp, tgt, mask, real_vocab=v)
+            lpm, _, _, _ = o.fwd(xm, tgt, mask, real_vocab=v)
+            fd[:, j] = g * (lpp - lpm) / (2 * h)
+        close(d[:, :v], fd, 1e-7)
+        act = mask & (tgt != IGNORE)
+        assert np.all(d[~act] == 0.0)
+        assert np.all(np.abs(d.sum(axis=1)) <= 1e-12 * (1 + np.abs(g)))
+        # autograd in float64
+        xt = torch.from_numpy(x).requires_grad_(True)
+        ls = torch.log_softmax(xt, dim=1)
+        sel = ls[torch.arange(n), torch.from_numpy(np.where(act, tgt, 0)).long()]
+        (sel * torch.from_numpy(np.where(act, g, 0.0))).sum().backward()
+        close(d[:, :v], xt.grad.numpy(), 1e-12)
+        # brute probabilities
+        close(d, brute.bwd(x.tolist(), tgt, mask, g, v, v + 3), 1e-12)
+
+
+def pin_partials(o):
+    rng = np.random.default_rng(17)
+    for v_real, v_pad, t in ((5, 5, 2), (3, 8, 4), (100, 128, 8), (64, 64, 64), (17, 24, 5)):
+        n = 4
+        bits = random_bf16(rng, (n, v_pad))
+        bits[1, :] = bf16_bits([-np.inf])[0]  # all -inf row
+        bits[:, v_real:] = 0x7FC0  # NaN in padding never counts
+        pm, ps = o.tile_partials(bits, real_vocab=v_real, padded_vocab=v_pad, num_tiles=t)
+        b = o.tile_bounds(v_pad, t)
+        x = decode(bits)
+        for r in range(n):
+            ref = brute.partials(x[r].tolist(), b.tolist(), v_real)
+            close(pm[r], [m for m, _ in ref], 1e-12)
+            close(ps[r], [s for _, s in ref], 1e-12)
+            for tt, (m, s) in enumerate(ref):
+                if m == -math.inf:  # identity partial, exactly
+                    assert pm[r, tt] == -math.inf and ps[r, tt] == 0.0
+    # the decomposition is an exact regrouping: merging the partials in
+    # ascending tile order reproduces the full-row LSE
+    n, v = 8, 151936
+    bits = random_bf16(rng, (n, v))
+    pm, ps = o.tile_partials(bits, real_vocab=v, padded_vocab=v, num_tiles=64)
+    _, lse, _, _ = o.fwd(bits, np.zeros(n, np.int32), None, real_vocab=v)
+    for r in range(n):
+        mm = max(pm[r])
+        merged = mm + math.log(math.fsum(s * math.exp(m - mm) for m, s in zip(pm[r], ps[r])))
+        assert abs(merged - lse[r]) <= 1e-12
+
+
+def pin_errors_and_nonfinite(o):
+    v, v_pad = 50, 56
+    rng = np.random.default_rng(19)
+    bits = random_bf16(rng, (6, v_pad))
+    tgt = np.array([0, -1, v, v_pad - 1, 3, 4], dtype=np.int32)
+    mask = np.array([1, 0, 1, 1, 1, 1], dtype=bool)
+    logp, lse, rc, bad = o.fwd(bits, tgt, mask, real_vocab=v, raise_on_error=False)
+    assert rc == oracle.ERR_TARGET_RANGE and bad == 2
+    assert np.isnan(logp[2]) and np.isnan(logp[3]) and logp[1] == 0.0
+    assert np.isfinite(lse).all()
+    with pytest.raises(oracle.OracleError):
+        o.fwd(bits, tgt, mask, real_vocab=v)
+    # non-finite LSE: all -inf row (active -> error, inactive -> fine)
+    b2 = random_bf16(rng, (3, v))
+    b2[1, :] = bf16_bits([-np.inf])[0]
+    _, ls, rc, bad = o.fwd(b2, np.zeros(3, np.int32), None, real_vocab=v, raise_on_error=False)
+    assert rc == oracle.ERR_NONFINITE_LSE and bad == 1 and ls[1] == -math.inf
+    _, ls, rc, _ = o.fwd(b2, np.zeros(3, np.int32), np.array([1, 0, 1]), real_vocab=v)
+    assert rc == 0 and ls[1] == -math.inf
+    # NaN or +inf among the real columns: LSE is NaN
+    b3 = random_bf16(rng, (3, v))
+    b3[0, 7] = 0x7FC0
+    b3[1, 9] = bf16_bits([np.inf])[0]
+    _, ls, _, _ = o.fwd(b3, np.zeros(3, np.int32), np.zeros(3), real_vocab=v)
+    assert np.isnan(ls[0]) and np.isnan(ls[1]) and np.isfinite(ls[2])
+    # empty batch
+    lp, ls, rc, _ = o.fwd(np.zeros((0, 8), np.uint16), np.zeros(0, np.int32), None, real_vocab=8)
+    assert rc == 0 and lp.shape == (0,)
+
+
+def pin_padding_and_ld(o):
+    rng = np.random.default_rng(23)
+    n, v_real, v_pad, ld = 5, 37, 40, 48
+    clean = random_bf16(rng, (n, ld))
+    clean[:, v_real:] = 0
+    dirty = clean.copy()
+    dirty[:, v_real:] = rng.integers(0, 65536, size=(n, ld - v_real)).astype(np.uint16)
+    tgt = rng.integers(0, v_real, size=n).astype(np.int32)
+    a = o.fwd(clean, tgt, None, real_vocab=v_real)
+    b = o.fwd(dirty, tgt, None, real_vocab=v_real)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # rows are read at stride ld: compare with the compact copy
+    compact = np.ascontiguousarray(clean[:, :v_real])
+    c = o.fwd(compact, tgt, None, real_vocab=v_real)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+    g = rng.normal(size=n)
+    d1 = o.bwd(dirty, tgt, None, a[1], g, real_vocab=v_real, padded_vocab=v_pad)
+    d2 = o.bwd(compact, tgt, None, a[1], g, real_vocab=v_real, padded_vocab=v_pad)
+    assert np.array_equal(d1, d2) and np.all(d1[:, v_real:] == 0.0)
+
+
+PINS = [pin_bf16_decode, pin_geometry, pin_fwd_brute, pin_closed_forms, pin_library,
+        pin_gradient, pin_partials, pin_errors_and_nonfinite, pin_padding_and_ld]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build(force=False)
+    return oracle.get()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(orc, pin):
+    pin(orc)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle source must fail some pin
+# --------------------------------------------------------------------------
+MUTANTS = {
+    "dropped_last_term": ("for (int64_t j = 0; j < n; ++j) sum += exp(x[j] - m);",
+                          "for (int64_t j = 0; j + 1 < n; ++j) sum += exp(x[j] - m);"),
+    "gradient_sign": ("d[j] = g * (onehot - exp(x[j] - lse));",
+                      "d[j] = g * (exp(x[j] - lse) - onehot);"),
+    "target_off_by_one": ("jb->logp[r] = x[t] - lse;",
+                          "jb->logp[r] = x[t > 0 ? t - 1 : t] - lse;"),
+    "row_stride_transposed": ("if (jb->xd) return jb->xd + r * jb->ld;\n"
+                              "  decode_row(jb->xb + r * jb->ld, n, scratch);",
+                              "if (jb->xd) return jb->xd + r * jb->real_vocab;\n"
+                              "  decode_row(jb->xb + r * jb->real_vocab, n, scratch);"),
+    "mask_ignored": ("int m = mask ? (mask[r] != 0) : 1;", "int m = 1; (void)mask;"),
+    "padding_counted": ("if (hi > jb->real_vocab) hi = jb->real_vocab;", ""),
+    "bf16_shift": ("uint32_t w = (uint32_t)bits << 16;", "uint32_t w = (uint32_t)bits << 15;"),
+    "bounds_truncated": ("bounds[t] = (padded_vocab * (int64_t)t) / (int64_t)num_tiles;",
+                         "bounds[t] = (padded_vocab / (int64_t)num_tiles) * (int64_t)t;"),
+    "onehot_dropped": ("double onehot = (j == (int64_t)t) ? 1.0 : 0.0;",
+                       "double onehot = 0.0;"),
+    "identity_partial_wrong": ("double m = -INFINITY, s = 0.0;", "double m = -INFINITY, s = 1.0;"),
+    "lse_unshifted_max": ("return m + log(sum);", "return log(sum);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(tmp_path: Path, name):
+    old, new = MUTANTS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.compile_oracle(mutant_src, tmp_path / f"lib_{name}.so")
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, oracle.OracleError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
