@@ -1,0 +1,229 @@
+"""Benchmark: one step = forward (per-tile partials + fixed-order merge + gather)
+plus backward (dlogits) over the large synthetic workload, on one MI355X.
+
+Prints ONE JSON line on stdout.  Everything else goes to stderr.
+
+  value        algorithmic GB/s of the whole step (logits read twice -- forward
+               and backward -- plus the dlogits write and the per-row vectors),
+               inputs resident in HBM before the timed region starts
+  roofline     the dominant kernel (by time): algorithmic bytes per launch over
+               its average launch time, measured with HIP events on the stream
+               the kernels run on; traffic = HBM bytes per launch from rocprofv3
+               FETCH_SIZE / WRITE_SIZE counters (committed under profiles/),
+               reported only while the kernel source is unchanged since then
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "logits GB/s + tokens/s, fwd+bwd selected-token logp, V=151936; % HBM peak"
+KERNEL_SOURCE = ROOT / "vocab_selected_token_amd" / "csrc" / "rlk_kernels.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_large_32k.txt"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, n_active: int) -> dict:
+    """Bytes the step must move at minimum (1 GB = 1e9 B).
+
+    forward : every real logit once (2 B) + per row: target 4, mask 1, logp 4, LSE 4
+    backward: real logits of effective-active rows (2 B) + every [N, V_pad] dlogit
+              written + per row: target 4, mask 1, LSE 4, g 4
+    """
+    n = wl.num_tokens
+    out_b = 2 if wl.dlogits_dtype == "bf16" else 4
+    fwd = n * wl.real_vocab * 2 + 13 * n
+    bwd = n_active * wl.real_vocab * 2 + n * wl.padded_vocab * out_b + 13 * n
+    return {"fwd": fwd, "bwd": bwd}
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    vals = {}
+    for line in TRAFFIC_FILE.read_text().splitlines():
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    key = f"{kernel}_hbm_bytes_per_launch"
+    return float(vals[key]) if key in vals else None
+
+
+def cpu_baseline(inp, wl, max_seconds: float) -> dict:
+    """The oracle (fp64 C, one thread per core) on leading rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    orc = oracle.get()
+    cores = max(1, min(16, os.cpu_count() or 1))
+    block = 256
+    done_rows, elapsed, bytes_done = 0, 0.0, 0.0
+    while done_rows < wl.num_tokens and elapsed < max_seconds:
+        rows = np.arange(done_rows, min(wl.num_tokens, done_rows + block))
+        bits, tgt, mask, g = W.to_host(inp, rows)
+        act = mask & (tgt != W.IGNORE_INDEX)
+        t0 = time.perf_counter()
+        _, lse, _, _ = orc.fwd(bits, tgt, mask, real_vocab=wl.real_vocab, nthreads=cores,
+                               raise_on_error=False)
+        orc.bwd(bits, tgt, mask, lse, g, real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                nthreads=cores, raise_on_error=False)
+        elapsed += time.perf_counter() - t0
+        sub = W.Workload(wl.name, 1, len(rows), wl.real_vocab, wl.padded_vocab, wl.sigma,
+                         dlogits_dtype=wl.dlogits_dtype)
+        b = algorithmic_bytes(sub, int(act.sum()))
+        bytes_done += b["fwd"] + b["bwd"]
+        done_rows += len(rows)
+    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"rows 0..{done_rows - 1} of the same workload ({done_rows} of "
+                      f"{wl.num_tokens} rows), fwd+bwd in fp64, {elapsed:.1f} s",
+            "tokens_per_s": round(done_rows / elapsed, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_bwd_b8s4096_v151936_p152576")
+    ap.add_argument("--shards", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="also run an untimed plain copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path is single-device by design", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    import vocab_selected_token_amd as rlk
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"bench: workload {wl.name}, generating inputs on {torch.cuda.get_device_name(dev)}")
+    inp = W.make_inputs(wl, dev)
+    n = wl.num_tokens
+    act = inp.mask & (inp.targets != W.IGNORE_INDEX)
+    n_active = int(act.sum())
+    nb = algorithmic_bytes(wl, n_active)
+
+    desc = rlk.make_desc(n, wl.real_vocab, wl.padded_vocab, wl.ld_logits, wl.num_tiles,
+                         args.shards, W.IGNORE_INDEX)
+    ws = rlk.workspace_for(desc, dev)
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    out_dt = torch.bfloat16 if wl.dlogits_dtype == "bf16" else torch.float32
+    ld_d = (wl.padded_vocab + 7) // 8 * 8
+    dl = torch.empty((n, ld_d), dtype=out_dt, device=dev) if wl.backward else None
+    code = rlk.RLK_DTYPE_BF16 if out_dt == torch.bfloat16 else rlk.RLK_DTYPE_F32
+    mask_u8 = inp.mask.view(torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        rlk.rlk_logp_fwd(desc, inp.logits, inp.targets, mask_u8, logp, lse, ws, stream)
+        if events:
+            events[1].record(stream)
+        if wl.backward:
+            rlk.rlk_logp_bwd(desc, inp.logits, inp.targets, mask_u8, lse, inp.grad, dl, ld_d,
+                             code, ws, stream)
+        if events:
+            events[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if wl.backward else 0.0
+    log(f"bench: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms)")
+
+    if args.copy_probe_gib > 0:  # plain copy kernel of known size, for counter scaling
+        nbytes = int(args.copy_probe_gib * 2 ** 30)
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy probe {nbytes} bytes x3 done")
+        del src, dst
+
+    total_bytes = nb["fwd"] + (nb["bwd"] if wl.backward else 0)
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+    fwd_gbs = nb["fwd"] / (fwd_ms * 1e-3) / 1e9
+    kernels = {"stage1_partials+stage2_merge": {"ms": round(fwd_ms, 4), "GB/s": round(fwd_gbs, 1),
+                                                "bytes": nb["fwd"]}}
+    if wl.backward:
+        bwd_gbs = nb["bwd"] / (bwd_ms * 1e-3) / 1e9
+        kernels["bwd_dlogits"] = {"ms": round(bwd_ms, 4), "GB/s": round(bwd_gbs, 1),
+                                  "bytes": nb["bwd"]}
+    dom = "bwd_dlogits" if wl.backward and bwd_ms >= fwd_ms else "stage1_partials+stage2_merge"
+    dom_gbs = kernels[dom]["GB/s"]
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic("bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
+                "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "input_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": n, "active_tokens": n_active,
+                   "real_vocab": wl.real_vocab, "padded_vocab": wl.padded_vocab,
+                   "vocab_tiles": wl.num_tiles, "virtual_shards": args.shards,
+                   "dlogits_dtype": wl.dlogits_dtype, "parallelism": "single-gpu"},
+        "tokens_per_s": round(n / (ms_step * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": total_bytes,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,209 @@
+"""Host-side checks of the C-ABI library (no GPU: nothing here launches a kernel).
+
+* the library loads and exports every function include/rlk_logp.h declares;
+* descriptor / pointer / size validation returns the documented status codes
+  before anything is enqueued;
+* the host geometry helper agrees with the oracle's geometry and with the
+  pages' sizes (64 tiles of 2374 columns over 151936, of 2384 over 152576).
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+import vocab_selected_token_amd as rlk
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "rlk_logp.h"
+
+
+def declared_functions() -> set[str]:
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(rlk_[a-z0-9_]+)\s*\(", text))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == set(rlk.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(rlk.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(rlk.LIB_PATH)], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert declared_functions() <= exported
+
+
+def test_library_does_not_link_the_oracle():
+    out = subprocess.run(["nm", "-D", str(rlk.LIB_PATH)], check=True, capture_output=True,
+                         text=True).stdout
+    assert "rlk_oracle" not in out
+    deps = subprocess.run(["ldd", str(rlk.LIB_PATH)], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+def desc(**kw):
+    base = dict(num_tokens=4, real_vocab=1000, padded_vocab=1024, ld_logits=1024,
+                num_vocab_tiles=64, num_virtual_shards=1, ignore_index=-100, validate=False)
+    base.update(kw)
+    return rlk.make_desc(**base)
+
+
+def test_workspace_bytes():
+    d = desc(num_tokens=32, num_vocab_tiles=64)
+    part = (32 * 64 * 4 + 255) // 256 * 256
+    assert rlk.rlk_logp_workspace_bytes(d) == 256 + 2 * part
+    d = desc(num_tokens=3, num_vocab_tiles=5)
+    assert rlk.rlk_logp_workspace_bytes(d) == 256 + 2 * 256
+    assert rlk.rlk_logp_workspace_bytes(desc(num_tokens=0)) == 256
+    assert rlk.rlk_logp_workspace_bytes(desc(num_vocab_tiles=0)) == 0
+
+
+BAD_DESCS = [
+    (dict(num_tokens=-1), rlk.RLK_ERR_BAD_SHAPE),
+    (dict(num_tokens=2 ** 31), rlk.RLK_ERR_BAD_SHAPE),
+    (dict(real_vocab=0), rlk.RLK_ERR_BAD_SHAPE),
+    (dict(real_vocab=2000), rlk.RLK_ERR_BAD_SHAPE),  # > padded
+    (dict(padded_vocab=2 ** 31, ld_logits=2 ** 31), rlk.RLK_ERR_BAD_SHAPE),
+    (dict(ld_logits=1016), rlk.RLK_ERR_BAD_SHAPE),  # < padded
+    (dict(ld_logits=1028), rlk.RLK_ERR_ALIGNMENT),
+    (dict(num_vocab_tiles=0), rlk.RLK_ERR_BAD_TILING),
+    (dict(num_vocab_tiles=1025), rlk.RLK_ERR_BAD_TILING),
+    (dict(num_virtual_shards=0), rlk.RLK_ERR_BAD_TILING),
+    (dict(num_virtual_shards=65), rlk.RLK_ERR_BAD_TILING),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DESCS)
+def test_fwd_rejects_bad_descriptor_before_launch(kw, code):
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_fwd(desc(**kw), None, None, None, None, None, None, stream=_NoStream())
+    assert ei.value.status == code
+    assert ei.value.detail
+
+
+class _NoStream:
+    """A stream stand-in: validation errors return before the stream is used."""
+    cuda_stream = 0
+
+
+class _FakeTensor:
+    """A pointer stand-in (never dereferenced: every case fails validation first)."""
+
+    def __init__(self, addr, nbytes=0):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def test_unknown_flags_and_null_desc():
+    d = desc()
+    d.flags = 0x80
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_fwd(d, None, None, None, None, None, None, stream=_NoStream())
+    assert ei.value.status == rlk.RLK_ERR_BAD_SHAPE
+    lib = ctypes.CDLL(str(rlk.LIB_PATH))
+    lib.rlk_logp_fwd.restype = ctypes.c_int
+    assert lib.rlk_logp_fwd(None, None, None, None, None, None, None, ctypes.c_size_t(0),
+                            None) == rlk.RLK_ERR_NULL_POINTER
+    lib.rlk_logp_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.rlk_logp_workspace_bytes(None) == 0
+
+
+def test_empty_batch_is_a_no_op():
+    rlk.rlk_logp_fwd(desc(num_tokens=0), None, None, None, None, None, None, stream=_NoStream())
+    rlk.rlk_logp_bwd(desc(num_tokens=0), None, None, None, None, None, None, 1024,
+                     rlk.RLK_DTYPE_F32, None, stream=_NoStream())
+
+
+def test_fwd_pointer_workspace_and_alignment_errors():
+    d = desc()
+    need = rlk.rlk_logp_workspace_bytes(d)
+    a = _FakeTensor(0x10000000)
+    ws = _FakeTensor(0x20000000, need)
+    s = _NoStream()
+    cases = [
+        ((None, a, None, a, a, ws), rlk.RLK_ERR_NULL_POINTER),
+        ((a, None, None, a, a, ws), rlk.RLK_ERR_NULL_POINTER),
+        ((a, a, None, None, a, ws), rlk.RLK_ERR_NULL_POINTER),
+        ((a, a, None, a, a, None), rlk.RLK_ERR_WORKSPACE),
+        ((a, a, None, a, a, _FakeTensor(0x20000000, need - 1)), rlk.RLK_ERR_WORKSPACE),
+        ((_FakeTensor(0x10000008), a, None, a, a, ws), rlk.RLK_ERR_ALIGNMENT),
+        ((a, a, None, a, a, _FakeTensor(0x20000080, need)), rlk.RLK_ERR_ALIGNMENT),
+        ((a, _FakeTensor(0x10000002), None, a, a, ws), rlk.RLK_ERR_ALIGNMENT),
+    ]
+    for args, code in cases:
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_fwd(d, *args, stream=s)
+        assert ei.value.status == code, (args, ei.value)
+
+
+def test_bwd_argument_errors():
+    d = desc()
+    a = _FakeTensor(0x10000000)
+    ws = _FakeTensor(0x20000000, 256)
+    s = _NoStream()
+    cases = [
+        (dict(ld=1024, dt=7), rlk.RLK_ERR_DTYPE),
+        (dict(ld=1016, dt=rlk.RLK_DTYPE_F32), rlk.RLK_ERR_BAD_SHAPE),
+        (dict(ld=1028, dt=rlk.RLK_DTYPE_BF16), rlk.RLK_ERR_ALIGNMENT),
+    ]
+    for kw, code in cases:
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_bwd(d, a, a, None, a, a, a, kw["ld"], kw["dt"], ws, stream=s)
+        assert ei.value.status == code
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_bwd(d, a, a, None, a, None, a, 1024, rlk.RLK_DTYPE_F32, ws, stream=s)
+    assert ei.value.status == rlk.RLK_ERR_NULL_POINTER
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_bwd(d, a, a, None, a, a, a, 1024, rlk.RLK_DTYPE_F32,
+                         _FakeTensor(0x20000000, 255), stream=s)
+    assert ei.value.status == rlk.RLK_ERR_WORKSPACE
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_bwd(d, a, a, None, a, a, _FakeTensor(0x30000004), 1024, rlk.RLK_DTYPE_F32,
+                         ws, stream=s)
+    assert ei.value.status == rlk.RLK_ERR_ALIGNMENT
+
+
+def test_status_strings():
+    for code in range(10):
+        assert rlk.rlk_status_string(code).startswith("RLK_")
+    assert rlk.rlk_status_string(rlk.RLK_ERR_TARGET_RANGE) == "RLK_ERR_TARGET_RANGE"
+    assert rlk.rlk_status_string(99) == "RLK_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("v_pad,t,s", [(151936, 64, 1), (152576, 64, 8), (10, 3, 2),
+                                       (1000, 7, 3), (17, 17, 5), (5, 1, 1)])
+def test_geometry_matches_oracle_and_pages(v_pad, t, s):
+    bounds, first = rlk.rlk_logp_tile_geometry(v_pad, t, s)
+    o = oracle.get()
+    assert np.array_equal(np.array(bounds), o.tile_bounds(v_pad, t))
+    assert np.array_equal(np.array(first), o.shard_tiles(t, s))
+    if (v_pad, t) == (151936, 64):
+        assert set(np.diff(bounds)) == {2374}
+    if (v_pad, t) == (152576, 64):
+        assert set(np.diff(bounds)) == {2384}
+
+
+def test_geometry_errors():
+    for args, code in (((0, 1, 1), rlk.RLK_ERR_BAD_SHAPE), ((10, 11, 1), rlk.RLK_ERR_BAD_TILING),
+                       ((10, 4, 5), rlk.RLK_ERR_BAD_TILING)):
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_tile_geometry(*args)
+        assert ei.value.status == code

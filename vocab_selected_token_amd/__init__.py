@@ -1,0 +1,188 @@
+"""Python binding of librlk_logp.so: deterministic selected-token logp on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/rlk_logp.h``; PyTorch supplies
+device memory and the stream.  There is no fallback: if the library is not
+built, importing this package raises.
+
+Functions with the C names take caller-allocated tensors and mirror the C
+signatures.  ``forward`` / ``backward`` are conveniences that allocate the
+outputs and workspace with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "librlk_logp.so"
+
+RLK_OK = 0
+RLK_ERR_NULL_POINTER = 1
+RLK_ERR_BAD_SHAPE = 2
+RLK_ERR_BAD_TILING = 3
+RLK_ERR_ALIGNMENT = 4
+RLK_ERR_WORKSPACE = 5
+RLK_ERR_DTYPE = 6
+RLK_ERR_TARGET_RANGE = 7
+RLK_ERR_NONFINITE_LSE = 8
+RLK_ERR_HIP = 9
+
+RLK_DTYPE_F32 = 0
+RLK_DTYPE_BF16 = 1
+RLK_FLAG_VALIDATE = 1
+
+EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd", "rlk_logp_tile_geometry",
+            "rlk_status_string", "rlk_last_error_detail")
+
+
+class rlk_logp_desc(ctypes.Structure):  # noqa: N801 - mirrors the C struct name
+    _fields_ = [("num_tokens", ctypes.c_int64), ("real_vocab", ctypes.c_int64),
+                ("padded_vocab", ctypes.c_int64), ("ld_logits", ctypes.c_int64),
+                ("num_vocab_tiles", ctypes.c_int32), ("num_virtual_shards", ctypes.c_int32),
+                ("ignore_index", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class RlkError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_lib.rlk_status_string(status).decode()}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is not built; run vocab_selected_token_amd.build_lib "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    dp = ctypes.POINTER(rlk_logp_desc)
+    lib.rlk_logp_workspace_bytes.argtypes = [dp]
+    lib.rlk_logp_workspace_bytes.restype = sz
+    lib.rlk_logp_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_fwd.restype = ctypes.c_int
+    lib.rlk_logp_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz, vp]
+    lib.rlk_logp_bwd.restype = ctypes.c_int
+    lib.rlk_logp_tile_geometry.argtypes = [i64, i32, i32, vp, vp]
+    lib.rlk_logp_tile_geometry.restype = ctypes.c_int
+    lib.rlk_status_string.argtypes = [ctypes.c_int]
+    lib.rlk_status_string.restype = ctypes.c_char_p
+    lib.rlk_last_error_detail.argtypes = []
+    lib.rlk_last_error_detail.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != RLK_OK:
+        raise RlkError(status, _lib.rlk_last_error_detail().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_desc(num_tokens: int, real_vocab: int, padded_vocab: int, ld_logits: int,
+              num_vocab_tiles: int = 64, num_virtual_shards: int = 1, ignore_index: int = -100,
+              validate: bool = False) -> rlk_logp_desc:
+    return rlk_logp_desc(num_tokens, real_vocab, padded_vocab, ld_logits, num_vocab_tiles,
+                         num_virtual_shards, ignore_index,
+                         RLK_FLAG_VALIDATE if validate else 0)
+
+
+# -- the C entry points --------------------------------------------------------
+def rlk_logp_workspace_bytes(desc: rlk_logp_desc) -> int:
+    return int(_lib.rlk_logp_workspace_bytes(ctypes.byref(desc)))
+
+
+def rlk_logp_fwd(desc, logits, targets, active_mask, logp, lse, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_fwd(ctypes.byref(desc), _ptr(logits), _ptr(targets), _ptr(active_mask),
+                             _ptr(logp), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_bwd(desc, logits, targets, active_mask, lse, grad_logp, dlogits, ld_dlogits: int,
+                 dlogits_dtype: int, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_bwd(ctypes.byref(desc), _ptr(logits), _ptr(targets), _ptr(active_mask),
+                             _ptr(lse), _ptr(grad_logp), _ptr(dlogits), ld_dlogits,
+                             dlogits_dtype, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_tile_geometry(padded_vocab: int, num_vocab_tiles: int, num_virtual_shards: int = 1):
+    """Host-only: (tile bounds [T+1] int64, shard first tiles [S+1] int32) as lists."""
+    b = (ctypes.c_int64 * (num_vocab_tiles + 1))() if num_vocab_tiles >= 1 else None
+    f = (ctypes.c_int32 * (num_virtual_shards + 1))() if num_virtual_shards >= 1 else None
+    _check(_lib.rlk_logp_tile_geometry(padded_vocab, num_vocab_tiles, num_virtual_shards,
+                                       ctypes.cast(b, ctypes.c_void_p) if b else None,
+                                       ctypes.cast(f, ctypes.c_void_p) if f else None))
+    return list(b), list(f)
+
+
+def rlk_status_string(status: int) -> str:
+    return _lib.rlk_status_string(status).decode()
+
+
+def rlk_last_error_detail() -> str:
+    return _lib.rlk_last_error_detail().decode()
+
+
+# -- conveniences: allocate outputs with torch, then call the C entry points ----
+def _u8_mask(mask):
+    if mask is None:
+        return None
+    return mask.view(torch.uint8) if mask.dtype == torch.bool else mask
+
+
+def workspace_for(desc: rlk_logp_desc, device) -> torch.Tensor:
+    n = rlk_logp_workspace_bytes(desc)
+    if n == 0:
+        _check(RLK_ERR_BAD_SHAPE)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def forward(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *, real_vocab: int,
+            padded_vocab: int | None = None, num_vocab_tiles: int = 64,
+            num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
+            workspace: torch.Tensor | None = None, stream=None):
+    """(logp, lse), fp32 [N] each.  logits: bf16 [N, ld] with unit column stride."""
+    n = logits.shape[0]
+    desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
+                     num_vocab_tiles, num_virtual_shards, ignore_index, validate)
+    logp = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if workspace is None:
+        workspace = workspace_for(desc, logits.device)
+    rlk_logp_fwd(desc, logits, targets, _u8_mask(active_mask), logp, lse, workspace, stream)
+    return logp, lse
+
+
+def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torch.Tensor,
+             grad_logp: torch.Tensor, *, real_vocab: int, padded_vocab: int | None = None,
+             out_dtype=torch.float32, ignore_index: int = -100, validate: bool = False,
+             num_vocab_tiles: int = 64, workspace: torch.Tensor | None = None, stream=None):
+    """dlogits [N, V_pad] (fp32 or bf16)."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    n = logits.shape[0]
+    v_pad = padded_vocab or logits.shape[1]
+    desc = make_desc(n, real_vocab, v_pad, logits.stride(0), num_vocab_tiles, 1, ignore_index,
+                     validate)
+    ld_d = (v_pad + 7) // 8 * 8
+    dl = torch.empty((n, ld_d), dtype=out_dtype, device=logits.device)
+    if workspace is None:
+        workspace = workspace_for(desc, logits.device)
+    code = RLK_DTYPE_BF16 if out_dtype == torch.bfloat16 else RLK_DTYPE_F32
+    rlk_logp_bwd(desc, logits, targets, _u8_mask(active_mask), lse, grad_logp, dl, ld_d, code,
+                 workspace, stream)
+    return dl[:, :v_pad]

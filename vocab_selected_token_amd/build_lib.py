@@ -1,0 +1,46 @@
+"""Build step for librlk_logp.so (hipcc, gfx950 only).
+
+Run ``python -m vocab_selected_token_amd.build_lib`` (or ``__graft_entry__.build()``).
+The library is built in-tree so that it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "librlk_logp.so"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -ffp-contract=off: only the explicit fmaf calls fuse, so every tile's
+# arithmetic is fixed by the source.  Packed fp32 VALU ops are disabled.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build() -> Path:
+    """Compile the kernels (HIP, gfx950) and the boundary (host C++) and link the library."""
+    obj_dir = PKG / "_build"
+    obj_dir.mkdir(exist_ok=True)
+    inc = [f"-I{ROOT / 'include'}", f"-I{CSRC}"]
+    k_obj = obj_dir / "rlk_kernels.o"
+    b_obj = obj_dir / "rlk_boundary.o"
+    subprocess.run([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / "rlk_kernels.hip"),
+                    "-o", str(k_obj)], check=True)
+    subprocess.run([HIPCC, "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", *inc, "-c", str(CSRC / "rlk_boundary.cpp"),
+                    "-o", str(b_obj)], check=True)
+    tmp = LIB.with_name(LIB.name + ".tmp")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", str(k_obj), str(b_obj),
+                    "-o", str(tmp)], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())
+    sys.exit(0)

@@ -1,0 +1,286 @@
+// rlk_boundary.cpp -- the C ABI of librlk_logp.so (declared in include/rlk_logp.h).
+//
+// Validates every descriptor field, pointer and size on the host before
+// anything is enqueued, derives the tile / virtual-shard geometry, and
+// launches the kernels of rlk_kernels.hip on the caller's stream.  The
+// library allocates nothing; its only state is the per-thread detail string.
+//
+// Error semantics follow PR #289 "[WS2][PR4][Logp] feat: add distributed TP/CP
+// logprob drift report": dispatch is fail-closed (PR1 commit messages: no
+// silent fallback), and the op rejects active targets outside the real
+// vocabulary and a non-finite logsumexp on an active row (review excerpt of
+// the op's apply()).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "rlk_internal.h"
+#include "rlk_logp.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+rlk_status fail(rlk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+rlk_status ok() { return RLK_OK; }
+
+constexpr size_t kStatusBytes = 256;
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validates the descriptor's sizes, tiling and flags.
+rlk_status check_desc(const rlk_logp_desc* d) {
+  if (!d) return fail(RLK_ERR_NULL_POINTER, "desc is NULL");
+  if (d->num_tokens < 0 || d->num_tokens > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "num_tokens=%lld outside [0, 2^31-1]",
+                (long long)d->num_tokens);
+  if (d->real_vocab < 1)
+    return fail(RLK_ERR_BAD_SHAPE, "real_vocab=%lld must be >= 1", (long long)d->real_vocab);
+  if (d->padded_vocab < d->real_vocab)
+    return fail(RLK_ERR_BAD_SHAPE, "padded_vocab=%lld < real_vocab=%lld",
+                (long long)d->padded_vocab, (long long)d->real_vocab);
+  if (d->padded_vocab > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "padded_vocab=%lld exceeds 2^31-1",
+                (long long)d->padded_vocab);
+  if (d->ld_logits < d->padded_vocab)
+    return fail(RLK_ERR_BAD_SHAPE, "ld_logits=%lld < padded_vocab=%lld",
+                (long long)d->ld_logits, (long long)d->padded_vocab);
+  if (d->ld_logits % 8 != 0)
+    return fail(RLK_ERR_ALIGNMENT, "ld_logits=%lld is not a multiple of 8 elements",
+                (long long)d->ld_logits);
+  if (d->num_vocab_tiles < 1 || (int64_t)d->num_vocab_tiles > d->padded_vocab)
+    return fail(RLK_ERR_BAD_TILING, "num_vocab_tiles=%d outside [1, padded_vocab=%lld]",
+                d->num_vocab_tiles, (long long)d->padded_vocab);
+  if (d->num_virtual_shards < 1 || d->num_virtual_shards > d->num_vocab_tiles)
+    return fail(RLK_ERR_BAD_TILING, "num_virtual_shards=%d outside [1, num_vocab_tiles=%d]",
+                d->num_virtual_shards, d->num_vocab_tiles);
+  if (d->flags & ~RLK_FLAG_VALIDATE)
+    return fail(RLK_ERR_BAD_SHAPE, "unknown flag bits 0x%x", d->flags & ~RLK_FLAG_VALIDATE);
+  // the partials must be addressable: N * T * 4 bytes, twice
+  if ((double)d->num_tokens * (double)d->num_vocab_tiles * 8.0 > 9.0e18)
+    return fail(RLK_ERR_BAD_SHAPE, "num_tokens * num_vocab_tiles too large");
+  return RLK_OK;
+}
+
+size_t partial_bytes(const rlk_logp_desc* d) {
+  return round256((size_t)d->num_tokens * (size_t)d->num_vocab_tiles * sizeof(float));
+}
+
+size_t needed_workspace(const rlk_logp_desc* d) { return kStatusBytes + 2 * partial_bytes(d); }
+
+rlk_status hip_fail(hipError_t e, const char* what) {
+  return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// With RLK_FLAG_VALIDATE: wait for the stream, then read the status words.
+rlk_status finish_validate(uint32_t* status, hipStream_t stream, bool check_nonfinite) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t host[2] = {0, 0};
+  e = hipMemcpy(host, status, sizeof host, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(status)");
+  if (host[0])
+    return fail(RLK_ERR_TARGET_RANGE,
+                "an effective-active target is outside [0, real_vocab); its outputs are NaN");
+  if (check_nonfinite && host[1])
+    return fail(RLK_ERR_NONFINITE_LSE,
+                "non-finite logsumexp on an effective-active row: logits over the real "
+                "vocabulary must be finite for every active token");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rlk_logp_workspace_bytes(const rlk_logp_desc* desc) {
+  if (check_desc(desc) != RLK_OK) return 0;
+  return needed_workspace(desc);
+}
+
+rlk_status rlk_logp_tile_geometry(int64_t padded_vocab, int32_t num_vocab_tiles,
+                                  int32_t num_virtual_shards, int64_t* bounds,
+                                  int32_t* shard_first_tile) {
+  if (padded_vocab < 1 || padded_vocab > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "padded_vocab=%lld outside [1, 2^31-1]",
+                (long long)padded_vocab);
+  if (num_vocab_tiles < 1 || (int64_t)num_vocab_tiles > padded_vocab)
+    return fail(RLK_ERR_BAD_TILING, "num_vocab_tiles=%d outside [1, padded_vocab]",
+                num_vocab_tiles);
+  if (num_virtual_shards < 1 || num_virtual_shards > num_vocab_tiles)
+    return fail(RLK_ERR_BAD_TILING, "num_virtual_shards=%d outside [1, num_vocab_tiles]",
+                num_virtual_shards);
+  if (bounds)
+    for (int32_t t = 0; t <= num_vocab_tiles; ++t)
+      bounds[t] = ((int64_t)t * padded_vocab) / num_vocab_tiles;
+  if (shard_first_tile)
+    for (int32_t s = 0; s <= num_virtual_shards; ++s)
+      shard_first_tile[s] = (int32_t)(((int64_t)s * num_vocab_tiles) / num_virtual_shards);
+  return ok();
+}
+
+rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, float* logp, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_desc(desc);
+  if (st != RLK_OK) return st;
+  const int64_t n = desc->num_tokens;
+  if (n == 0) return ok();
+  if (!logits || !targets || !logp || !lse)
+    return fail(RLK_ERR_NULL_POINTER, "logits, targets, logp and lse must be non-NULL");
+  if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < needed_workspace(desc))
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes,
+                needed_workspace(desc));
+  if (!aligned(logits, 16)) return fail(RLK_ERR_ALIGNMENT, "logits not 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, logp and lse must be 4-byte aligned");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  const int32_t T = desc->num_vocab_tiles, S = desc->num_virtual_shards;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  float* pmax = reinterpret_cast<float*>(ws + kStatusBytes);
+  float* psum = reinterpret_cast<float*>(ws + kStatusBytes + partial_bytes(desc));
+  const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
+
+  hipError_t e;
+  if (validate) {
+    e = rlk::launch_clear_status(status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+  }
+  rlk::Stage1Args a1;
+  a1.logits = logits;
+  a1.ld = desc->ld_logits;
+  a1.num_rows = (int32_t)n;
+  a1.real_vocab = (int32_t)desc->real_vocab;
+  a1.padded_vocab = (int32_t)desc->padded_vocab;
+  a1.num_tiles = T;
+  a1.tile_width = (desc->padded_vocab % T == 0) ? (int32_t)(desc->padded_vocab / T) : 0;
+  a1.pmax = pmax;
+  a1.psum = psum;
+  for (int32_t s = 0; s < S; ++s) {  // one launch per virtual shard
+    const int32_t t0 = (int32_t)(((int64_t)s * T) / S);
+    const int32_t t1 = (int32_t)(((int64_t)(s + 1) * T) / S);
+    a1.tile_begin = t0;
+    a1.tile_count = t1 - t0;
+    if (rlk::stage1_blocks((int64_t)n * a1.tile_count) > kI32Max)
+      return fail(RLK_ERR_BAD_SHAPE, "num_tokens * tiles per shard too large for one launch");
+    e = rlk::launch_stage1(a1, stream);
+    if (e != hipSuccess) return hip_fail(e, "stage1_partials launch");
+  }
+  rlk::Stage2Args a2;
+  a2.logits = logits;
+  a2.ld = desc->ld_logits;
+  a2.num_rows = (int32_t)n;
+  a2.real_vocab = (int32_t)desc->real_vocab;
+  a2.num_tiles = T;
+  a2.pmax = pmax;
+  a2.psum = psum;
+  a2.targets = targets;
+  a2.mask = active_mask;
+  a2.ignore_index = desc->ignore_index;
+  a2.logp = logp;
+  a2.lse = lse;
+  a2.status = status;
+  e = rlk::launch_stage2(a2, stream);
+  if (e != hipSuccess) return hip_fail(e, "stage2_merge launch");
+  if (validate) return finish_validate(status, stream, true);
+  return ok();
+}
+
+rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, const float* lse, const float* grad_logp,
+                        void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_desc(desc);
+  if (st != RLK_OK) return st;
+  if (dlogits_dtype != RLK_DTYPE_F32 && dlogits_dtype != RLK_DTYPE_BF16)
+    return fail(RLK_ERR_DTYPE, "dlogits_dtype=%d is neither RLK_DTYPE_F32 nor RLK_DTYPE_BF16",
+                (int)dlogits_dtype);
+  if (ld_dlogits < desc->padded_vocab)
+    return fail(RLK_ERR_BAD_SHAPE, "ld_dlogits=%lld < padded_vocab=%lld", (long long)ld_dlogits,
+                (long long)desc->padded_vocab);
+  if (ld_dlogits % 8 != 0)
+    return fail(RLK_ERR_ALIGNMENT, "ld_dlogits=%lld is not a multiple of 8 elements",
+                (long long)ld_dlogits);
+  const int64_t n = desc->num_tokens;
+  if (n == 0) return ok();
+  if (!logits || !targets || !lse || !grad_logp || !dlogits)
+    return fail(RLK_ERR_NULL_POINTER, "logits, targets, lse, grad_logp and dlogits must be "
+                                      "non-NULL");
+  if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < kStatusBytes)
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < %zu", workspace_bytes, kStatusBytes);
+  if (!aligned(logits, 16) || !aligned(dlogits, 16))
+    return fail(RLK_ERR_ALIGNMENT, "logits and dlogits must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, lse and grad_logp must be 4-byte aligned");
+  if (n * rlk::bwd_col_blocks((int32_t)desc->padded_vocab) > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "num_tokens * column blocks too large for one launch");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint32_t* status = reinterpret_cast<uint32_t*>(workspace);
+  const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
+  hipError_t e;
+  if (validate) {
+    e = rlk::launch_clear_status(status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+  }
+  rlk::BwdArgs a;
+  a.logits = logits;
+  a.ld = desc->ld_logits;
+  a.num_rows = (int32_t)n;
+  a.real_vocab = (int32_t)desc->real_vocab;
+  a.padded_vocab = (int32_t)desc->padded_vocab;
+  a.targets = targets;
+  a.mask = active_mask;
+  a.ignore_index = desc->ignore_index;
+  a.lse = lse;
+  a.grad = grad_logp;
+  a.dlogits = dlogits;
+  a.ld_d = ld_dlogits;
+  a.out_bf16 = dlogits_dtype == RLK_DTYPE_BF16;
+  a.status = status;
+  e = rlk::launch_bwd(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "bwd_dlogits launch");
+  if (validate) return finish_validate(status, stream, false);
+  return ok();
+}
+
+const char* rlk_status_string(rlk_status s) {
+  switch (s) {
+    case RLK_OK: return "RLK_OK";
+    case RLK_ERR_NULL_POINTER: return "RLK_ERR_NULL_POINTER";
+    case RLK_ERR_BAD_SHAPE: return "RLK_ERR_BAD_SHAPE";
+    case RLK_ERR_BAD_TILING: return "RLK_ERR_BAD_TILING";
+    case RLK_ERR_ALIGNMENT: return "RLK_ERR_ALIGNMENT";
+    case RLK_ERR_WORKSPACE: return "RLK_ERR_WORKSPACE";
+    case RLK_ERR_DTYPE: return "RLK_ERR_DTYPE";
+    case RLK_ERR_TARGET_RANGE: return "RLK_ERR_TARGET_RANGE";
+    case RLK_ERR_NONFINITE_LSE: return "RLK_ERR_NONFINITE_LSE";
+    case RLK_ERR_HIP: return "RLK_ERR_HIP";
+  }
+  return "RLK_ERR_UNKNOWN";
+}
+
+const char* rlk_last_error_detail(void) { return g_detail.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,422 @@
+// rlk_kernels.hip -- gfx950 kernels for deterministic selected-token logp.
+//
+// Three kernels, one per step of the path:
+//   stage1_partials  per (row, vocab tile) fp32 (max, sumexp) over the tile's
+//                    real columns ("masked per-tile partials").
+//   stage2_merge     per row: merge the T partials in ascending tile order into
+//                    LSE, gather the target logit, apply the active mask and
+//                    ignore_index, flag bad targets / non-finite LSE.
+//   bwd_dlogits      dX = g * (onehot - exp(X - LSE)) on effective-active rows.
+//
+// Sources (web pages, by title and section): PR #289 "[WS2][PR4][Logp] feat:
+// add distributed TP/CP logprob drift report", stacked PR1 commit messages
+// (padded columns masked to -inf before the local (max, sumexp) partials; the
+// (-inf, 0) identity partial; fp32 merge in fixed global tile order; fp32 logp
+// and LSE outputs) and the review excerpt of the op's apply() (active-target
+// range check, non-finite-LSE check).  Issue #323 "[WS2][Logprob] H100
+// validation and reproduction guide for Issue #241 PR1-PR5", "4. Cross-Topology
+// Bitwise Check" (outputs identical whatever the tile grouping).
+//
+// Determinism: no atomics; every tile is reduced by the same 16-lane lane
+// mapping (lane l of the group takes the tile's full 16-byte chunks l, l+16,
+// ...) and the same fixed DPP tree whatever launch or shard computes it; the
+// merge runs in ascending tile order.  The file is built with
+// -ffp-contract=off so that only the fmaf calls written here fuse.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_internal.h"
+
+namespace rlk {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
+
+// Stage-1 geometry: a wave of 64 lanes reduces 4 tiles at once, 16 lanes
+// (one DPP row) per tile; each lane holds kChunks 16-byte chunks per pass.
+constexpr int kGroupLanes = 16;
+constexpr int kGroupsPerWave = 4;
+constexpr int kWavesPerBlock = 4;
+constexpr int kChunks = 5;
+constexpr int kPassChunks = kChunks * kGroupLanes;  // 80 chunks = 640 columns
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// NaN-propagating maximum (IEEE 754-2019 maximum).
+__device__ __forceinline__ float maxnan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rotate right by N lanes within each row of 16 lanes (DPP row_ror:N).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Fold 8 unpacked values into a lane's running (m, s) pair; the values are a
+// pass of kChunks*8 columns held in registers (max first, then the sum).
+template <int NV>
+__device__ __forceinline__ void fold_values(const float (&v)[NV], float& m, float& s) {
+  float bm = v[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) bm = maxnan(bm, v[i]);
+  const float nm = maxnan(m, bm);
+  if (nm == kNegInf) return;  // everything so far is -inf: (m, s) stays (-inf, 0)
+  // rescale the running sum to the new max (exp2(0) == 1 leaves it unchanged)
+  s = s * exp2_hw((m - nm) * kLog2e);
+  const float nml = nm;
+#pragma unroll
+  for (int c = 0; c < NV / 8; ++c) {
+    float cs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs += exp2_hw((v[c * 8 + e] - nml) * kLog2e);
+    s += cs;
+  }
+  m = nm;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& q, float* v) {
+  v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+  v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+  v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1: masked per-tile partials.
+//   logits      [N, ld] bf16 as 16-byte chunks (ld_chunks = ld / 8)
+//   tiles       [tile_begin, tile_begin + tile_count) of T, for every row
+//   tile_width  V_pad / T when T divides V_pad, else 0 (floor formula)
+//   pmax, psum  [N][T] fp32
+// Work item i = row * tile_count + (tile - tile_begin); group q of wave w
+// takes item 4w + q.  Columns >= V_real never enter the arithmetic; chunks
+// that straddle a tile bound are masked by column index.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stage1_partials(
+    const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
+    int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t tile_begin,
+    int32_t tile_count, float* __restrict__ pmax, float* __restrict__ psum) {
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4;
+  const int gl = lane & 15;
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block) * kGroupsPerWave;
+  const int64_t n_items = (int64_t)num_rows * tile_count;
+
+  // item -> (row, tile) once per wave on the scalar unit, then step by grp
+  int32_t row = (int32_t)(item0 / tile_count);
+  int32_t tq = (int32_t)(item0 - (int64_t)row * tile_count) + grp;
+  while (tq >= tile_count) {
+    tq -= tile_count;
+    ++row;
+  }
+  const bool have = item0 + grp < n_items;
+  const int32_t tile = tile_begin + tq;
+
+  int32_t lo = 0, hi = 0;
+  if (have) {
+    if (tile_width) {
+      lo = tile * tile_width;
+      hi = lo + tile_width;
+    } else {
+      lo = (int32_t)(((int64_t)tile * padded_vocab) / num_tiles);
+      hi = (int32_t)(((int64_t)(tile + 1) * padded_vocab) / num_tiles);
+    }
+    if (hi > real_vocab) hi = real_vocab;  // padded columns never count
+    if (hi < lo) hi = lo;                  // an all-padding tile is empty
+  }
+  const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
+
+  float m = kNegInf, s = 0.0f;
+
+  // chunks cut by a tile bound: the head (lo not 16-byte aligned) goes to
+  // lane 0 of the group, the tail (hi not aligned) to lane 1
+  const int32_t cf_lo = (lo + 7) >> 3;  // first full chunk
+  int32_t cf_hi = hi >> 3;              // end of full chunks
+  if (cf_hi < cf_lo) cf_hi = cf_lo;
+  {
+    int32_t c = -1, e_lo = 0, e_hi = 0;
+    if (gl == 0 && hi > lo && (lo & 7)) {
+      c = lo >> 3;
+      e_lo = lo & 7;
+      e_hi = min(hi - (c << 3), 8);
+    } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= cf_lo) {
+      c = hi >> 3;
+      e_lo = 0;
+      e_hi = hi & 7;
+    }
+    if (c >= 0) {
+      float v[8];
+      unpack8(rowp[c], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < e_lo || e >= e_hi) v[e] = kNegInf;
+      fold_values(v, m, s);
+    }
+  }
+
+  // full chunks [cf_lo, cf_hi): whole passes first, then a remainder pass
+  int32_t base = cf_lo;
+  for (; base + kPassChunks <= cf_hi; base += kPassChunks) {
+    uint4 q[kChunks];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) q[k] = rowp[base + k * kGroupLanes + gl];
+    float v[kChunks * 8];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
+    fold_values(v, m, s);
+  }
+  if (base < cf_hi) {
+    uint4 q[kChunks];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int32_t c = base + k * kGroupLanes + gl;
+      q[k] = rowp[min(c, cf_hi - 1)];
+      if (c >= cf_hi) q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+    }
+    float v[kChunks * 8];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
+    fold_values(v, m, s);
+  }
+
+  // combine the 16 lanes of the group: exact max, then a fixed rotate tree
+  float gm = m;
+  gm = maxnan(gm, row_ror<8>(gm));
+  gm = maxnan(gm, row_ror<4>(gm));
+  gm = maxnan(gm, row_ror<2>(gm));
+  gm = maxnan(gm, row_ror<1>(gm));
+  float ls = 0.0f;
+  if (gm != kNegInf && m != kNegInf) ls = s * exp2_hw((m - gm) * kLog2e);
+  ls += row_ror<8>(ls);
+  ls += row_ror<4>(ls);
+  ls += row_ror<2>(ls);
+  ls += row_ror<1>(ls);
+  if (gm == kNegInf) ls = 0.0f;  // the (-inf, 0) identity partial
+
+  if (have && gl == 0) {
+    const int64_t o = (int64_t)row * num_tiles + tile;
+    pmax[o] = gm;
+    psum[o] = ls;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: per-row merge in ascending tile order, target gather, mask.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stage2_merge(
+    const uint16_t* __restrict__ logits, int64_t ld, int32_t num_rows, int32_t real_vocab,
+    int32_t num_tiles, const float* __restrict__ pmax, const float* __restrict__ psum,
+    const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
+    float* __restrict__ logp, float* __restrict__ lse, uint32_t* __restrict__ status) {
+  const int32_t r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= num_rows) return;
+  const float* pm = pmax + (int64_t)r * num_tiles;
+  const float* ps = psum + (int64_t)r * num_tiles;
+  float M = kNegInf;
+  for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
+  float L = kNegInf;
+  if (M != kNegInf) {
+    float S = 0.0f;
+    for (int32_t t = 0; t < num_tiles; ++t) {
+      const float mt = pm[t];
+      if (mt != kNegInf) S = fmaf(ps[t], expf(mt - M), S);
+    }
+    L = M + logf(S);
+  }
+  lse[r] = L;
+
+  const bool act = (mask == nullptr || mask[r] != 0);
+  const int32_t tgt = act ? targets[r] : 0;
+  if (!act || tgt == ignore_index) {
+    logp[r] = 0.0f;
+    return;
+  }
+  if (tgt < 0 || tgt >= real_vocab) {
+    logp[r] = __builtin_nanf("");
+    status[0] = 1u;
+    return;
+  }
+  const float x = __uint_as_float((uint32_t)logits[(int64_t)r * ld + tgt] << 16);
+  logp[r] = x - L;
+  if (!__builtin_isfinite(L)) status[1] = 1u;
+}
+
+// ---------------------------------------------------------------------------
+// Backward: one block covers kBwdCols consecutive columns of one row.
+// ---------------------------------------------------------------------------
+constexpr int kBwdThreads = 256;
+constexpr int kBwdUnroll = 4;
+constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 8192 columns
+
+template <typename OutT>
+struct Store8;
+
+template <>
+struct Store8<float> {
+  // out points at the chunk's first column; n = columns to write (1..8)
+  static __device__ __forceinline__ void store(float* out, const float* d, int n) {
+    if (n == 8) {
+      reinterpret_cast<float4*>(out)[0] = make_float4(d[0], d[1], d[2], d[3]);
+      reinterpret_cast<float4*>(out)[1] = make_float4(d[4], d[5], d[6], d[7]);
+    } else {
+      for (int e = 0; e < n; ++e) out[e] = d[e];
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  // two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+template <>
+struct Store8<uint16_t> {
+  static __device__ __forceinline__ void store(uint16_t* out, const float* d, int n) {
+    const uint4 w = make_uint4(pack_bf16_rne(d[0], d[1]), pack_bf16_rne(d[2], d[3]),
+                               pack_bf16_rne(d[4], d[5]), pack_bf16_rne(d[6], d[7]));
+    if (n == 8) {
+      *reinterpret_cast<uint4*>(out) = w;
+    } else {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int e = 0; e < n; ++e) out[e] = (uint16_t)(ws[e >> 1] >> ((e & 1) * 16));
+    }
+  }
+};
+
+template <typename OutT>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
+    const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
+    int32_t padded_vocab, int32_t col_blocks, const int32_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, int32_t ignore_index, const float* __restrict__ lse,
+    const float* __restrict__ grad, OutT* __restrict__ dlogits, int64_t ld_d,
+    uint32_t* __restrict__ status) {
+  const int32_t row = blockIdx.x / col_blocks;
+  const int32_t cb = blockIdx.x - row * col_blocks;
+  const bool act_mask = (mask == nullptr || mask[row] != 0);
+  const int32_t tgt = act_mask ? targets[row] : 0;
+  const bool act = act_mask && tgt != ignore_index;
+  const bool bad = act && (tgt < 0 || tgt >= real_vocab);
+  if (bad && cb == 0 && threadIdx.x == 0) status[0] = 1u;
+  const float L = act ? lse[row] : 0.0f;
+  const float g = act ? grad[row] : 0.0f;
+  OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
+  const uint4* __restrict__ xrow = logits + (int64_t)row * ld_chunks;
+  const int32_t c0 = cb * (kBwdCols / 8) + threadIdx.x;
+
+  uint4 q[kBwdUnroll];
+  if (act && !bad) {
+#pragma unroll
+    for (int k = 0; k < kBwdUnroll; ++k) {
+      const int32_t c = c0 + k * kBwdThreads;
+      if ((c << 3) < real_vocab) q[k] = xrow[c];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kBwdUnroll; ++k) {
+    const int32_t c = c0 + k * kBwdThreads;
+    const int32_t j0 = c << 3;
+    if (j0 >= padded_vocab) continue;
+    float d[8];
+    if (!act) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    } else if (bad) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
+    } else if (j0 >= real_vocab) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    } else {
+      float x[8];
+      unpack8(q[k], x);
+      const float ng = -g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
+      if (j0 + 8 > real_vocab) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (j0 + e >= real_vocab) d[e] = 0.0f;
+      }
+      if (tgt >= j0 && tgt < j0 + 8) {
+        const int e = tgt - j0;
+        d[e] = g * (1.0f - exp2_hw((x[e] - L) * kLog2e));
+      }
+    }
+    Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
+  }
+}
+
+__global__ void clear_status(uint32_t* status) {
+  if (threadIdx.x < 2) status[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers (called by the boundary after it has validated every argument).
+// ---------------------------------------------------------------------------
+int64_t stage1_blocks(int64_t items) {
+  const int64_t per_block = (int64_t)kWavesPerBlock * kGroupsPerWave;
+  return (items + per_block - 1) / per_block;
+}
+
+hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.num_rows * a.tile_count;
+  if (items == 0) return hipSuccess;
+  const dim3 grid((unsigned)stage1_blocks(items));
+  hipLaunchKernelGGL(stage1_partials, grid, dim3(kWavesPerBlock * 64), 0, stream,
+                     reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
+                     a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
+                     a.tile_count, a.pmax, a.psum);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.num_rows + 255) / 256));
+  hipLaunchKernelGGL(stage2_merge, grid, dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(a.logits), a.ld, a.num_rows, a.real_vocab,
+                     a.num_tiles, a.pmax, a.psum, a.targets, a.mask, a.ignore_index, a.logp,
+                     a.lse, a.status);
+  return hipGetLastError();
+}
+
+int64_t bwd_col_blocks(int32_t padded_vocab) {
+  return ((int64_t)padded_vocab + kBwdCols - 1) / kBwdCols;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  const int32_t cbs = (int32_t)bwd_col_blocks(a.padded_vocab);
+  const dim3 grid((unsigned)((int64_t)a.num_rows * cbs));
+  const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  if (a.out_bf16) {
+    hipLaunchKernelGGL(bwd_dlogits<uint16_t>, grid, dim3(kBwdThreads), 0, stream, x, a.ld / 8,
+                       a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets, a.mask,
+                       a.ignore_index, a.lse, a.grad, reinterpret_cast<uint16_t*>(a.dlogits),
+                       a.ld_d, a.status);
+  } else {
+    hipLaunchKernelGGL(bwd_dlogits<float>, grid, dim3(kBwdThreads), 0, stream, x, a.ld / 8,
+                       a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets, a.mask,
+                       a.ignore_index, a.lse, a.grad, reinterpret_cast<float*>(a.dlogits),
+                       a.ld_d, a.status);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_status, dim3(1), dim3(64), 0, stream, status);
+  return hipGetLastError();
+}
+
+}  // namespace rlk
