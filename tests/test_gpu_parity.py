@@ -47,7 +47,7 @@ def bwd(inp, lse, dtype, validate=False):
     wl = inp.wl
     return rlk.backward(inp.logits, inp.targets, inp.mask, lse, inp.grad,
                         real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab, out_dtype=dtype,
-                        validate=validate)
+                        validate=validate, num_vocab_tiles=wl.num_tiles)
 
 
 def raw_bits(d: torch.Tensor) -> np.ndarray:

@@ -147,7 +147,7 @@ def _u8_mask(mask):
 def workspace_for(desc: rlk_logp_desc, device) -> torch.Tensor:
     n = rlk_logp_workspace_bytes(desc)
     if n == 0:
-        _check(RLK_ERR_BAD_SHAPE)
+        raise ValueError(f"invalid rlk_logp_desc: {rlk_last_error_detail()}")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -170,14 +170,15 @@ def forward(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *, re
 def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torch.Tensor,
              grad_logp: torch.Tensor, *, real_vocab: int, padded_vocab: int | None = None,
              out_dtype=torch.float32, ignore_index: int = -100, validate: bool = False,
-             num_vocab_tiles: int = 64, workspace: torch.Tensor | None = None, stream=None):
+             num_vocab_tiles: int | None = None, workspace: torch.Tensor | None = None,
+             stream=None):
     """dlogits [N, V_pad] (fp32 or bf16)."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
-    desc = make_desc(n, real_vocab, v_pad, logits.stride(0), num_vocab_tiles, 1, ignore_index,
-                     validate)
+    tiles = num_vocab_tiles if num_vocab_tiles is not None else min(64, v_pad)
+    desc = make_desc(n, real_vocab, v_pad, logits.stride(0), tiles, 1, ignore_index, validate)
     ld_d = (v_pad + 7) // 8 * 8
     dl = torch.empty((n, ld_d), dtype=out_dtype, device=logits.device)
     if workspace is None:
