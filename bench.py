@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -51,7 +52,12 @@ def algorithmic_bytes(wl, n_active: int) -> dict:
 
 
 def kernel_source_sha() -> str:
-    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+    """Hash of the kernel source with comments and whitespace removed: it changes
+    exactly when the code the counters were taken on changes."""
+    text = KERNEL_SOURCE.read_text()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def read_traffic(kernel: str):

@@ -52,6 +52,29 @@ __device__ __forceinline__ float maxnan(float a, float b) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bytes of logits.  Streaming loads of the logits carry the nontemporal
+// hint: every byte is read once per kernel, so it should not displace lines
+// that neighbouring tiles will still use.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& w) {
+  __builtin_nontemporal_store(u32x4{w.x, w.y, w.z, w.w}, reinterpret_cast<u32x4*>(p));
+}
+
+// Block index -> work index so that consecutive work indices run on the same
+// XCD.  The hardware hands blocks to the 8 XCDs round-robin; each XCD has its
+// own L2, and neighbouring tiles share the 128-byte line at their bound, so
+// keeping a row's blocks on one XCD lets the second tile find that line in L2.
+// A bijection on [0, gridDim.x).
+__device__ __forceinline__ int64_t xcd_local_block(int64_t b, int64_t nb) {
+  constexpr int64_t kXcds = 8;
+  const int64_t per = nb / kXcds, rem = nb % kXcds, x = b % kXcds, l = b / kXcds;
+  return x * per + (x < rem ? x : rem) + l;
+}
+
 // Rotate right by N lanes within each row of 16 lanes (DPP row_ror:N).
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
@@ -94,8 +117,9 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
 //   tiles       [tile_begin, tile_begin + tile_count) of T, for every row
 //   tile_width  V_pad / T when T divides V_pad, else 0 (floor formula)
 //   pmax, psum  [N][T] fp32
-// Work item i = row * tile_count + (tile - tile_begin); group q of wave w
-// takes item 4w + q.  Columns >= V_real never enter the arithmetic; chunks
+// Work item i = row * tile_count + (tile - tile_begin); group q of wave w of
+// work block b (the XCD-local renumbering of blockIdx.x) takes item
+// 16b + 4w + q.  Columns >= V_real never enter the arithmetic; chunks
 // that straddle a tile bound are masked by column index.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void stage1_partials(
@@ -106,7 +130,8 @@ __global__ __launch_bounds__(256) void stage1_partials(
   const int grp = lane >> 4;
   const int gl = lane & 15;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block) * kGroupsPerWave;
+  const int64_t block = xcd_local_block(blockIdx.x, gridDim.x);
+  const int64_t item0 = (block * kWavesPerBlock + wave_in_block) * kGroupsPerWave;
   const int64_t n_items = (int64_t)num_rows * tile_count;
 
   // item -> (row, tile) once per wave on the scalar unit, then step by grp
@@ -153,7 +178,7 @@ __global__ __launch_bounds__(256) void stage1_partials(
     }
     if (c >= 0) {
       float v[8];
-      unpack8(rowp[c], v);
+      unpack8(load_stream(rowp + c), v);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < e_lo || e >= e_hi) v[e] = kNegInf;
@@ -166,7 +191,7 @@ __global__ __launch_bounds__(256) void stage1_partials(
   for (; base + kPassChunks <= cf_hi; base += kPassChunks) {
     uint4 q[kChunks];
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) q[k] = rowp[base + k * kGroupLanes + gl];
+    for (int k = 0; k < kChunks; ++k) q[k] = load_stream(rowp + base + k * kGroupLanes + gl);
     float v[kChunks * 8];
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
@@ -177,7 +202,7 @@ __global__ __launch_bounds__(256) void stage1_partials(
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
       const int32_t c = base + k * kGroupLanes + gl;
-      q[k] = rowp[min(c, cf_hi - 1)];
+      q[k] = load_stream(rowp + min(c, cf_hi - 1));
       if (c >= cf_hi) q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
     }
     float v[kChunks * 8];
@@ -252,8 +277,8 @@ __global__ __launch_bounds__(256) void stage2_merge(
 // Backward: one block covers kBwdCols consecutive columns of one row.
 // ---------------------------------------------------------------------------
 constexpr int kBwdThreads = 256;
-constexpr int kBwdUnroll = 4;
-constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 8192 columns
+constexpr int kBwdUnroll = 2;
+constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 4096 columns
 
 template <typename OutT>
 struct Store8;
@@ -263,8 +288,11 @@ struct Store8<float> {
   // out points at the chunk's first column; n = columns to write (1..8)
   static __device__ __forceinline__ void store(float* out, const float* d, int n) {
     if (n == 8) {
-      reinterpret_cast<float4*>(out)[0] = make_float4(d[0], d[1], d[2], d[3]);
-      reinterpret_cast<float4*>(out)[1] = make_float4(d[4], d[5], d[6], d[7]);
+      uint4* o = reinterpret_cast<uint4*>(out);
+      store_stream(o, make_uint4(__float_as_uint(d[0]), __float_as_uint(d[1]),
+                                 __float_as_uint(d[2]), __float_as_uint(d[3])));
+      store_stream(o + 1, make_uint4(__float_as_uint(d[4]), __float_as_uint(d[5]),
+                                     __float_as_uint(d[6]), __float_as_uint(d[7])));
     } else {
       for (int e = 0; e < n; ++e) out[e] = d[e];
     }
@@ -285,7 +313,7 @@ struct Store8<uint16_t> {
     const uint4 w = make_uint4(pack_bf16_rne(d[0], d[1]), pack_bf16_rne(d[2], d[3]),
                                pack_bf16_rne(d[4], d[5]), pack_bf16_rne(d[6], d[7]));
     if (n == 8) {
-      *reinterpret_cast<uint4*>(out) = w;
+      store_stream(reinterpret_cast<uint4*>(out), w);
     } else {
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
       for (int e = 0; e < n; ++e) out[e] = (uint16_t)(ws[e >> 1] >> ((e & 1) * 16));
