@@ -111,6 +111,25 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
   v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
 }
 
+// The last, partial pass over a tile's full chunks: K slots per lane, slot k
+// of lane gl is chunk base + 16k + gl when that is below cf_hi, else -inf.
+template <int K>
+__device__ __forceinline__ void remainder_pass(const uint4* __restrict__ rowp, int32_t base,
+                                               int32_t cf_hi, int gl, float& m, float& s) {
+  if (base >= cf_hi) return;  // this lane's tile has no remainder
+  uint4 q[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int32_t c = base + k * kGroupLanes + gl;
+    q[k] = load_stream(rowp + min(c, cf_hi - 1));
+    if (c >= cf_hi) q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+  }
+  float v[K * 8];
+#pragma unroll
+  for (int k = 0; k < K; ++k) unpack8(q[k], &v[k * 8]);
+  fold_values(v, m, s);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1: masked per-tile partials.
 //   logits      [N, ld] bf16 as 16-byte chunks (ld_chunks = ld / 8)
@@ -197,18 +216,19 @@ __global__ __launch_bounds__(256) void stage1_partials(
     for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
     fold_values(v, m, s);
   }
-  if (base < cf_hi) {
-    uint4 q[kChunks];
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int32_t c = base + k * kGroupLanes + gl;
-      q[k] = load_stream(rowp + min(c, cf_hi - 1));
-      if (c >= cf_hi) q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
-    }
-    float v[kChunks * 8];
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
-    fold_values(v, m, s);
+  // The remainder pass takes as many chunk slots per lane as the wave's
+  // widest remainder needs (1..kChunks).  Slots past cf_hi hold -inf and add
+  // exactly 0, so the slot count never changes a tile's result.
+  int32_t slots = base < cf_hi ? (cf_hi - base + kGroupLanes - 1) / kGroupLanes : 0;
+  slots = max(max(__builtin_amdgcn_readlane(slots, 0), __builtin_amdgcn_readlane(slots, 16)),
+              max(__builtin_amdgcn_readlane(slots, 32), __builtin_amdgcn_readlane(slots, 48)));
+  switch (slots) {
+    case 1: remainder_pass<1>(rowp, base, cf_hi, gl, m, s); break;
+    case 2: remainder_pass<2>(rowp, base, cf_hi, gl, m, s); break;
+    case 3: remainder_pass<3>(rowp, base, cf_hi, gl, m, s); break;
+    case 4: remainder_pass<4>(rowp, base, cf_hi, gl, m, s); break;
+    case 5: remainder_pass<5>(rowp, base, cf_hi, gl, m, s); break;
+    default: break;
   }
 
   // combine the 16 lanes of the group: exact max, then a fixed rotate tree
