@@ -111,18 +111,22 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
   v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
 }
 
-// The last, partial pass over a tile's full chunks: K slots per lane, slot k
-// of lane gl is chunk base + 16k + gl when that is below cf_hi, else -inf.
+// A pass with K chunk slots per lane in which some slots fall outside the
+// tile's full chunks [lo_c, hi_c): slot k of lane gl is chunk base + 16k + gl,
+// and slots outside the range hold -inf (they add exactly 0).  The load
+// address is clamped into the range, so nothing outside the tile is read.
 template <int K>
-__device__ __forceinline__ void remainder_pass(const uint4* __restrict__ rowp, int32_t base,
-                                               int32_t cf_hi, int gl, float& m, float& s) {
-  if (base >= cf_hi) return;  // this lane's tile has no remainder
+__device__ __forceinline__ void masked_pass(const uint4* __restrict__ rowp, int32_t base,
+                                            int32_t lo_c, int32_t hi_c, int gl, float& m,
+                                            float& s) {
+  if (base >= hi_c || lo_c >= hi_c) return;  // nothing of this lane's tile here
   uint4 q[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int32_t c = base + k * kGroupLanes + gl;
-    q[k] = load_stream(rowp + min(c, cf_hi - 1));
-    if (c >= cf_hi) q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+    q[k] = load_stream(rowp + min(max(c, lo_c), hi_c - 1));
+    if (c < lo_c || c >= hi_c)
+      q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
   }
   float v[K * 8];
 #pragma unroll
@@ -205,8 +209,17 @@ __global__ __launch_bounds__(256) void stage1_partials(
     }
   }
 
-  // full chunks [cf_lo, cf_hi): whole passes first, then a remainder pass
-  int32_t base = cf_lo;
+  // Full chunks [cf_lo, cf_hi).  Passes start on the 128-byte line (8 chunks,
+  // counted from the row start) that holds cf_lo, so that each 16-lane load
+  // covers whole lines and no line is split between two loads of a group; a
+  // leading pass masks the chunks in front of cf_lo.  Then whole passes, then
+  // a remainder pass of as many slots as the wave's widest remainder needs
+  // (1..kChunks).  The mapping depends only on the tile's columns.
+  int32_t base = cf_lo & ~7;
+  if (base < cf_lo) {
+    masked_pass<kChunks>(rowp, base, cf_lo, cf_hi, gl, m, s);
+    base += kPassChunks;
+  }
   for (; base + kPassChunks <= cf_hi; base += kPassChunks) {
     uint4 q[kChunks];
 #pragma unroll
@@ -216,18 +229,15 @@ __global__ __launch_bounds__(256) void stage1_partials(
     for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
     fold_values(v, m, s);
   }
-  // The remainder pass takes as many chunk slots per lane as the wave's
-  // widest remainder needs (1..kChunks).  Slots past cf_hi hold -inf and add
-  // exactly 0, so the slot count never changes a tile's result.
   int32_t slots = base < cf_hi ? (cf_hi - base + kGroupLanes - 1) / kGroupLanes : 0;
   slots = max(max(__builtin_amdgcn_readlane(slots, 0), __builtin_amdgcn_readlane(slots, 16)),
               max(__builtin_amdgcn_readlane(slots, 32), __builtin_amdgcn_readlane(slots, 48)));
   switch (slots) {
-    case 1: remainder_pass<1>(rowp, base, cf_hi, gl, m, s); break;
-    case 2: remainder_pass<2>(rowp, base, cf_hi, gl, m, s); break;
-    case 3: remainder_pass<3>(rowp, base, cf_hi, gl, m, s); break;
-    case 4: remainder_pass<4>(rowp, base, cf_hi, gl, m, s); break;
-    case 5: remainder_pass<5>(rowp, base, cf_hi, gl, m, s); break;
+    case 1: masked_pass<1>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
+    case 2: masked_pass<2>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
+    case 3: masked_pass<3>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
+    case 4: masked_pass<4>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
+    case 5: masked_pass<5>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
     default: break;
   }
 
