@@ -265,26 +265,57 @@ __global__ __launch_bounds__(256) void stage1_partials(
 // ---------------------------------------------------------------------------
 // Stage 2: per-row merge in ascending tile order, target gather, mask.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void stage2_merge(
+constexpr int kMergeThreads = 64;  // one row per lane; small blocks spread rows over every CU
+constexpr int kMergeVec = 64;      // tiles held in registers by the vectorised path
+
+// LSE from a row's T partials: exact max first, then the rescaled sum in
+// ascending tile order with fmaf, skipping identity partials; -inf if every
+// partial is the identity.  pm/ps point at the row's T values.
+__device__ __forceinline__ float merge_row(const float* __restrict__ pm,
+                                           const float* __restrict__ ps, int32_t num_tiles) {
+  if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
+    // same arithmetic, with the loads issued up front as 16-byte vectors
+    float mv[kMergeVec], sv[kMergeVec];
+#pragma unroll
+    for (int t = 0; t < kMergeVec; t += 4) {
+      if (t < num_tiles) {
+        const float4 a = *reinterpret_cast<const float4*>(pm + t);
+        const float4 b = *reinterpret_cast<const float4*>(ps + t);
+        mv[t] = a.x; mv[t + 1] = a.y; mv[t + 2] = a.z; mv[t + 3] = a.w;
+        sv[t] = b.x; sv[t + 1] = b.y; sv[t + 2] = b.z; sv[t + 3] = b.w;
+      }
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kMergeVec; ++t)
+      if (t < num_tiles) M = maxnan(M, mv[t]);
+    if (M == kNegInf) return kNegInf;
+    float S = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMergeVec; ++t)
+      if (t < num_tiles && mv[t] != kNegInf) S = fmaf(sv[t], expf(mv[t] - M), S);
+    return M + logf(S);
+  }
+  float M = kNegInf;
+  for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
+  if (M == kNegInf) return kNegInf;
+  float S = 0.0f;
+  for (int32_t t = 0; t < num_tiles; ++t) {
+    const float mt = pm[t];
+    if (mt != kNegInf) S = fmaf(ps[t], expf(mt - M), S);
+  }
+  return M + logf(S);
+}
+
+__global__ __launch_bounds__(kMergeThreads) void stage2_merge(
     const uint16_t* __restrict__ logits, int64_t ld, int32_t num_rows, int32_t real_vocab,
     int32_t num_tiles, const float* __restrict__ pmax, const float* __restrict__ psum,
     const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
     float* __restrict__ logp, float* __restrict__ lse, uint32_t* __restrict__ status) {
   const int32_t r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= num_rows) return;
-  const float* pm = pmax + (int64_t)r * num_tiles;
-  const float* ps = psum + (int64_t)r * num_tiles;
-  float M = kNegInf;
-  for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
-  float L = kNegInf;
-  if (M != kNegInf) {
-    float S = 0.0f;
-    for (int32_t t = 0; t < num_tiles; ++t) {
-      const float mt = pm[t];
-      if (mt != kNegInf) S = fmaf(ps[t], expf(mt - M), S);
-    }
-    L = M + logf(S);
-  }
+  const float L = merge_row(pmax + (int64_t)r * num_tiles, psum + (int64_t)r * num_tiles,
+                            num_tiles);
   lse[r] = L;
 
   const bool act = (mask == nullptr || mask[r] != 0);
@@ -306,9 +337,9 @@ __global__ __launch_bounds__(256) void stage2_merge(
 // ---------------------------------------------------------------------------
 // Backward: one block covers kBwdCols consecutive columns of one row.
 // ---------------------------------------------------------------------------
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 128;
 constexpr int kBwdUnroll = 2;
-constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 4096 columns
+constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 2048 columns
 
 template <typename OutT>
 struct Store8;
@@ -441,8 +472,8 @@ hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
 
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.num_rows + 255) / 256));
-  hipLaunchKernelGGL(stage2_merge, grid, dim3(256), 0, stream,
+  const dim3 grid((unsigned)((a.num_rows + kMergeThreads - 1) / kMergeThreads));
+  hipLaunchKernelGGL(stage2_merge, grid, dim3(kMergeThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(a.logits), a.ld, a.num_rows, a.real_vocab,
                      a.num_tiles, a.pmax, a.psum, a.targets, a.mask, a.ignore_index, a.logp,
                      a.lse, a.status);
