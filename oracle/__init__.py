@@ -104,6 +104,8 @@ class Oracle:
         part_args = [vp, i64, i64, i64, i64, i32, vp, vp, ctypes.c_int]
         lib.rlk_oracle_tile_partials_f64.argtypes = part_args
         lib.rlk_oracle_tile_partials_bf16.argtypes = part_args
+        lib.rlk_oracle_lmhead_logits.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, ctypes.c_int]
+        lib.rlk_oracle_lmhead_logits.restype = ctypes.c_int
         for name in ("rlk_oracle_tile_bounds", "rlk_oracle_shard_tiles", "rlk_oracle_fwd_f64",
                      "rlk_oracle_fwd_bf16", "rlk_oracle_bwd_f64", "rlk_oracle_bwd_bf16",
                      "rlk_oracle_tile_partials_f64", "rlk_oracle_tile_partials_bf16"):
@@ -165,6 +167,30 @@ class Oracle:
         if rc == ERR_ARG or (rc and raise_on_error):
             raise OracleError(rc, bad.value)
         return d
+
+    def lmhead_logits(self, h, w, *, real_vocab: int, nthreads: int = 0) -> np.ndarray:
+        """z = h . W^T in fp64 over W's first real_vocab rows.  h: [N, K], W: [V, K],
+        both bf16 bit patterns (uint16).  Returns [N, real_vocab] float64."""
+        h = np.ascontiguousarray(np.asarray(h))
+        w = np.ascontiguousarray(np.asarray(w))
+        if h.dtype != np.uint16 or w.dtype != np.uint16 or h.ndim != 2 or w.ndim != 2:
+            raise TypeError("h and W must be 2-D bf16 bit patterns (uint16)")
+        if h.shape[1] != w.shape[1] or w.shape[0] < real_vocab:
+            raise ValueError("h [N, K] and W [>= real_vocab, K] must share K")
+        n, k = h.shape
+        z = np.empty((n, real_vocab), dtype=np.float64)
+        rc = self._lib.rlk_oracle_lmhead_logits(_ptr(h), _ptr(w), n, k, real_vocab, k, k,
+                                                _ptr(z), nthreads)
+        if rc:
+            raise OracleError(rc, -1)
+        return z
+
+    def lmhead_fwd(self, h, w, tgt, mask=None, *, real_vocab: int, ignore_index: int = -100,
+                   nthreads: int = 0, raise_on_error: bool = True):
+        """Selected-token logp and LSE of z = h . W^T (fp64): (logp, lse, status, bad_row)."""
+        z = self.lmhead_logits(h, w, real_vocab=real_vocab, nthreads=nthreads)
+        return self.fwd(z, tgt, mask, real_vocab=real_vocab, ignore_index=ignore_index,
+                        nthreads=nthreads, raise_on_error=raise_on_error)
 
     def tile_partials(self, x, *, real_vocab: int, padded_vocab: int, num_tiles: int,
                       nthreads: int = 0):

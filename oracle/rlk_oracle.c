@@ -393,6 +393,89 @@ int rlk_oracle_bwd_bf16(const uint16_t* x, int64_t n_rows, int64_t real_vocab,
                   d, ldd, bad_row, nthreads);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Fused LM-head variant: the logits are z = h . W^T over the real vocabulary */
+/* rows of W, computed in fp64 from the bf16 inputs; the selected-token logp  */
+/* then follows from z exactly as for materialised logits (rlk_oracle_fwd_f64 */
+/* on z).  The pages name an optional fused kernel without describing it      */
+/* ([I323] "Validation Boundary": the optional PR6 fused kernel); the reading */
+/* here is the plain one: the same log-softmax, over logits that are a GEMM.  */
+/*   h  bf16 [n_rows, ld_h], K = hidden_dim <= ld_h                           */
+/*   W  bf16 [>= real_vocab rows, ld_w], K <= ld_w; rows >= real_vocab unread */
+/*   z  fp64 [n_rows, real_vocab] out                                         */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const uint16_t* h;
+  const uint16_t* w;
+  int64_t n_rows, k, real_vocab, ld_h, ld_w;
+  double* z;
+  int64_t r0, r1;
+  int status;
+} mm_job;
+
+static void* mm_block(void* arg) {
+  mm_job* jb = (mm_job*)arg;
+  double* hr = (double*)malloc(sizeof(double) * (size_t)(jb->k > 0 ? jb->k : 1));
+  double* wr = (double*)malloc(sizeof(double) * (size_t)(jb->k > 0 ? jb->k : 1));
+  if (!hr || !wr) {
+    free(hr);
+    free(wr);
+    jb->status = ORC_ERR_NOMEM;
+    return NULL;
+  }
+  for (int64_t r = jb->r0; r < jb->r1; ++r) {
+    decode_row(jb->h + r * jb->ld_h, jb->k, hr);
+    for (int64_t j = 0; j < jb->real_vocab; ++j) {
+      decode_row(jb->w + j * jb->ld_w, jb->k, wr);
+      double acc = 0.0;
+      for (int64_t q = 0; q < jb->k; ++q) acc += hr[q] * wr[q]; /* ascending k */
+      jb->z[r * jb->real_vocab + j] = acc;
+    }
+  }
+  free(hr);
+  free(wr);
+  return NULL;
+}
+
+int rlk_oracle_lmhead_logits(const uint16_t* h, const uint16_t* w, int64_t n_rows,
+                             int64_t hidden_dim, int64_t real_vocab, int64_t ld_h, int64_t ld_w,
+                             double* z, int nthreads) {
+  if (n_rows < 0 || hidden_dim < 1 || real_vocab < 1 || ld_h < hidden_dim || ld_w < hidden_dim)
+    return ORC_ERR_ARG;
+  if (n_rows == 0) return ORC_OK;
+  if (!h || !w || !z) return ORC_ERR_ARG;
+  if (nthreads <= 0) {
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    nthreads = n > 0 ? (int)n : 1;
+  }
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > n_rows) nthreads = (int)n_rows;
+  mm_job jobs[256];
+  pthread_t th[256];
+  int started[256];
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i].h = h;
+    jobs[i].w = w;
+    jobs[i].n_rows = n_rows;
+    jobs[i].k = hidden_dim;
+    jobs[i].real_vocab = real_vocab;
+    jobs[i].ld_h = ld_h;
+    jobs[i].ld_w = ld_w;
+    jobs[i].z = z;
+    jobs[i].r0 = n_rows * i / nthreads;
+    jobs[i].r1 = n_rows * (i + 1) / nthreads;
+    jobs[i].status = ORC_OK;
+    started[i] = (nthreads > 1) && pthread_create(&th[i], NULL, mm_block, &jobs[i]) == 0;
+    if (!started[i]) mm_block(&jobs[i]);
+  }
+  int status = ORC_OK;
+  for (int i = 0; i < nthreads; ++i) {
+    if (started[i]) pthread_join(th[i], NULL);
+    if (jobs[i].status != ORC_OK) status = jobs[i].status;
+  }
+  return status;
+}
+
 /* Per-tile (max, sumexp) partials, [N][T] row-major, by the plain definition
  * over each tile's real columns ([PR289] PR1 commit messages: padded columns
  * are masked before the local partials; a padding-only or all -inf tile gives

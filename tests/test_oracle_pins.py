@@ -297,8 +297,34 @@ def pin_padding_and_ld(o):
     assert np.array_equal(d1, d2) and np.all(d1[:, v_real:] == 0.0)
 
 
+def pin_lmhead(o):
+    """Fused LM-head logits: z = h . W^T in fp64 over real vocabulary rows."""
+    rng = np.random.default_rng(29)
+    n, k, v_real, v_pad = 7, 48, 123, 130
+    h = random_bf16(rng, (n, k), sigma=1.0)
+    w = random_bf16(rng, (v_pad, k), sigma=0.5)
+    w[v_real:] = 0x7FC0  # padding rows hold NaN and must never be read
+    z = o.lmhead_logits(h, w, real_vocab=v_real)
+    ref = decode(h) @ decode(w[:v_real]).T  # float64 library matmul
+    assert z.shape == (n, v_real) and np.isfinite(z).all()
+    assert np.max(np.abs(z - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # a one-hot hidden state selects one column of W, exactly
+    e = np.zeros((3, k), dtype=np.uint16)
+    for r, col in enumerate((0, 17, k - 1)):
+        e[r, col] = bf16_bits([1.0])[0]
+    z1 = o.lmhead_logits(e, w, real_vocab=v_real)
+    for r, col in enumerate((0, 17, k - 1)):
+        assert np.array_equal(z1[r], decode(w[:v_real, col]))
+    # the selected-token logp of the fused variant is the log-softmax of z
+    tgt = rng.integers(0, v_real, size=n).astype(np.int32)
+    lp, ls, _, _ = o.lmhead_fwd(h, w, tgt, real_vocab=v_real)
+    ls_ref = torch.logsumexp(torch.from_numpy(ref), dim=1).numpy()
+    close(ls, ls_ref, 1e-12)
+    close(lp, ref[np.arange(n), tgt] - ls_ref, 1e-12)
+
+
 PINS = [pin_bf16_decode, pin_geometry, pin_fwd_brute, pin_closed_forms, pin_library,
-        pin_gradient, pin_partials, pin_errors_and_nonfinite, pin_padding_and_ld]
+        pin_gradient, pin_partials, pin_errors_and_nonfinite, pin_padding_and_ld, pin_lmhead]
 
 
 @pytest.fixture(scope="module")
@@ -335,6 +361,10 @@ MUTANTS = {
                        "double onehot = 0.0;"),
     "identity_partial_wrong": ("double m = -INFINITY, s = 0.0;", "double m = -INFINITY, s = 1.0;"),
     "lse_unshifted_max": ("return m + log(sum);", "return log(sum);"),
+    "lmhead_dropped_k": ("for (int64_t q = 0; q < jb->k; ++q) acc += hr[q] * wr[q];",
+                         "for (int64_t q = 0; q + 1 < jb->k; ++q) acc += hr[q] * wr[q];"),
+    "lmhead_wrong_hidden_row": ("decode_row(jb->h + r * jb->ld_h, jb->k, hr);",
+                                "decode_row(jb->h + (r > 0 ? r - 1 : r) * jb->ld_h, jb->k, hr);"),
 }
 
 
