@@ -405,34 +405,32 @@ int rlk_oracle_bwd_bf16(const uint16_t* x, int64_t n_rows, int64_t real_vocab,
 /*   z  fp64 [n_rows, real_vocab] out                                         */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-  const uint16_t* h;
+  const double* hd;  /* decoded hidden rows, [n_rows][k] */
   const uint16_t* w;
-  int64_t n_rows, k, real_vocab, ld_h, ld_w;
+  int64_t n_rows, k, ld_w, real_vocab;
   double* z;
-  int64_t r0, r1;
+  int64_t j0, j1; /* this thread's vocabulary rows */
   int status;
 } mm_job;
 
+/* Threads split the vocabulary rows; each W row is decoded once and dotted
+ * with every hidden row, summing over k in ascending order. */
 static void* mm_block(void* arg) {
   mm_job* jb = (mm_job*)arg;
-  double* hr = (double*)malloc(sizeof(double) * (size_t)(jb->k > 0 ? jb->k : 1));
   double* wr = (double*)malloc(sizeof(double) * (size_t)(jb->k > 0 ? jb->k : 1));
-  if (!hr || !wr) {
-    free(hr);
-    free(wr);
+  if (!wr) {
     jb->status = ORC_ERR_NOMEM;
     return NULL;
   }
-  for (int64_t r = jb->r0; r < jb->r1; ++r) {
-    decode_row(jb->h + r * jb->ld_h, jb->k, hr);
-    for (int64_t j = 0; j < jb->real_vocab; ++j) {
-      decode_row(jb->w + j * jb->ld_w, jb->k, wr);
+  for (int64_t j = jb->j0; j < jb->j1; ++j) {
+    decode_row(jb->w + j * jb->ld_w, jb->k, wr);
+    for (int64_t r = 0; r < jb->n_rows; ++r) {
+      const double* hr = jb->hd + r * jb->k;
       double acc = 0.0;
       for (int64_t q = 0; q < jb->k; ++q) acc += hr[q] * wr[q]; /* ascending k */
       jb->z[r * jb->real_vocab + j] = acc;
     }
   }
-  free(hr);
   free(wr);
   return NULL;
 }
@@ -444,26 +442,28 @@ int rlk_oracle_lmhead_logits(const uint16_t* h, const uint16_t* w, int64_t n_row
     return ORC_ERR_ARG;
   if (n_rows == 0) return ORC_OK;
   if (!h || !w || !z) return ORC_ERR_ARG;
+  double* hd = (double*)malloc(sizeof(double) * (size_t)n_rows * (size_t)hidden_dim);
+  if (!hd) return ORC_ERR_NOMEM;
+  for (int64_t r = 0; r < n_rows; ++r) decode_row(h + r * ld_h, hidden_dim, hd + r * hidden_dim);
   if (nthreads <= 0) {
     long n = sysconf(_SC_NPROCESSORS_ONLN);
     nthreads = n > 0 ? (int)n : 1;
   }
   if (nthreads > 256) nthreads = 256;
-  if ((int64_t)nthreads > n_rows) nthreads = (int)n_rows;
+  if ((int64_t)nthreads > real_vocab) nthreads = (int)real_vocab;
   mm_job jobs[256];
   pthread_t th[256];
   int started[256];
   for (int i = 0; i < nthreads; ++i) {
-    jobs[i].h = h;
+    jobs[i].hd = hd;
     jobs[i].w = w;
     jobs[i].n_rows = n_rows;
     jobs[i].k = hidden_dim;
-    jobs[i].real_vocab = real_vocab;
-    jobs[i].ld_h = ld_h;
     jobs[i].ld_w = ld_w;
+    jobs[i].real_vocab = real_vocab;
     jobs[i].z = z;
-    jobs[i].r0 = n_rows * i / nthreads;
-    jobs[i].r1 = n_rows * (i + 1) / nthreads;
+    jobs[i].j0 = real_vocab * i / nthreads;
+    jobs[i].j1 = real_vocab * (i + 1) / nthreads;
     jobs[i].status = ORC_OK;
     started[i] = (nthreads > 1) && pthread_create(&th[i], NULL, mm_block, &jobs[i]) == 0;
     if (!started[i]) mm_block(&jobs[i]);
@@ -473,6 +473,7 @@ int rlk_oracle_lmhead_logits(const uint16_t* h, const uint16_t* w, int64_t n_row
     if (started[i]) pthread_join(th[i], NULL);
     if (jobs[i].status != ORC_OK) status = jobs[i].status;
   }
+  free(hd);
   return status;
 }
 

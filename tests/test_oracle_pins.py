@@ -363,8 +363,8 @@ MUTANTS = {
     "lse_unshifted_max": ("return m + log(sum);", "return log(sum);"),
     "lmhead_dropped_k": ("for (int64_t q = 0; q < jb->k; ++q) acc += hr[q] * wr[q];",
                          "for (int64_t q = 0; q + 1 < jb->k; ++q) acc += hr[q] * wr[q];"),
-    "lmhead_wrong_hidden_row": ("decode_row(jb->h + r * jb->ld_h, jb->k, hr);",
-                                "decode_row(jb->h + (r > 0 ? r - 1 : r) * jb->ld_h, jb->k, hr);"),
+    "lmhead_wrong_hidden_row": ("const double* hr = jb->hd + r * jb->k;",
+                                "const double* hr = jb->hd + (r > 0 ? r - 1 : r) * jb->k;"),
 }
 
 
