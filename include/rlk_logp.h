@@ -158,6 +158,33 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
                         void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Fused LM-head variant: the logits are z = hidden . weight^T, taken in fp32
+ * from bf16 MFMA products and never written to memory.  The pages name an
+ * optional fused kernel without describing it ([I323] "Validation Boundary");
+ * this one keeps [PR289]'s contract -- per-tile fp32 (max, sumexp) over the real
+ * columns, the (-inf, 0) identity, the merge in ascending tile order, fp32 logp
+ * and LSE -- with the statistics and the target logit read from the fp32
+ * accumulators (no rounding of z to bf16).
+ *   desc        num_tokens, real_vocab, padded_vocab, num_vocab_tiles,
+ *               ignore_index and flags as for rlk_logp_fwd; ld_logits is not
+ *               used; num_virtual_shards must be 1; every tile must be at least
+ *               256 columns wide (padded_vocab / num_vocab_tiles >= 256).
+ *   hidden      (device) bf16 [num_tokens, hidden_dim], row-major, 16-byte aligned.
+ *   weight      (device) bf16 [padded_vocab, hidden_dim], row-major, 16-byte
+ *               aligned; rows >= real_vocab are never read.
+ *   hidden_dim  a positive multiple of 64.
+ *   targets, active_mask, logp, lse   as for rlk_logp_fwd.
+ *   workspace   >= rlk_logp_fused_lmhead_workspace_bytes(desc), 256-byte
+ *               aligned.  Its status words and per-tile partials sit where
+ *               rlk_logp_fwd puts them; the rest is scratch.
+ * Errors as for rlk_logp_fwd; RLK_ERR_BAD_TILING also for tiles narrower than
+ * 256 columns or num_virtual_shards != 1. */
+size_t rlk_logp_fused_lmhead_workspace_bytes(const rlk_logp_desc* desc);
+rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
+                                 const void* weight, int64_t hidden_dim, const int32_t* targets,
+                                 const uint8_t* active_mask, float* logp, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only geometry (no device access): writes T+1 tile bounds
  * floor(t*V_pad/T) to `bounds` and S+1 shard starts floor(s*T/S) to
  * `shard_first_tile` (either may be NULL).  Same limits as the descriptor. */

@@ -1,0 +1,128 @@
+"""GPU parity of the fused LM-head variant against the oracle (z = h . W^T in
+fp64, then the full-vocabulary log-softmax).  Needs an MI355X."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_selected_token_amd as rlk
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda")
+IGNORE = -100
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_case(n, k, v_real, v_pad, seed, w_sigma=0.05, mask_keep=0.8, ignore_frac=0.1):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    h = torch.randn((n, k), generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((v_pad, k), generator=g, device=DEV) * w_sigma).to(torch.bfloat16)
+    if v_pad > v_real:  # padding rows hold garbage, and must never be read
+        w[v_real:] = torch.randint(-32768, 32768, (v_pad - v_real, k), generator=g, device=DEV,
+                                   dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    tgt = torch.randint(0, v_real, (n,), generator=g, device=DEV, dtype=torch.int32)
+    mask = torch.rand(n, generator=g, device=DEV) < mask_keep
+    tgt[torch.rand(n, generator=g, device=DEV) < ignore_frac] = IGNORE
+    return h, w, tgt, mask
+
+
+def run(h, w, tgt, mask, v_real, v_pad, tiles, validate=False):
+    n, k = h.shape
+    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, 1, IGNORE, validate)
+    ws = torch.empty(rlk.rlk_logp_fused_lmhead_workspace_bytes(desc), dtype=torch.uint8,
+                     device=DEV)
+    logp = torch.empty(n, device=DEV)
+    lse = torch.empty(n, device=DEV)
+    rlk.rlk_logp_fused_lmhead(desc, h, w, k, tgt, None if mask is None else mask.view(torch.uint8),
+                              logp, lse, ws)
+    torch.cuda.synchronize()
+    return logp, lse, ws
+
+
+CASES = [
+    dict(n=37, k=64, v_real=1000, v_pad=1024, tiles=4),
+    dict(n=300, k=128, v_real=2500, v_pad=2560, tiles=10),
+    dict(n=257, k=320, v_real=3000, v_pad=3000, tiles=7),
+    dict(n=1, k=64, v_real=256, v_pad=256, tiles=1),
+    dict(n=513, k=192, v_real=5000, v_pad=5120, tiles=3),
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=lambda c: "n{n}_k{k}_v{v_real}_p{v_pad}_T{tiles}".format(**c))
+def test_fused_small_parity(c):
+    print(f"case {c}", flush=True)
+    h, w, tgt, mask = make_case(c["n"], c["k"], c["v_real"], c["v_pad"], seed=c["n"])
+    logp, lse, ws = run(h, w, tgt, mask, c["v_real"], c["v_pad"], c["tiles"])
+    o = oracle.get()
+    hb, wb = bf16_bits(h), bf16_bits(w)
+    z = o.lmhead_logits(hb, wb, real_vocab=c["v_real"])
+    t_h, m_h = tgt.cpu().numpy(), mask.cpu().numpy()
+    lo, so, _, _ = o.fwd(z, t_h, m_h, real_vocab=c["v_real"])
+    act = P.effective_active(t_h, m_h)
+    P.check_fwd(logp.cpu().numpy(), lse.cpu().numpy(), lo, so, act, str(c))
+    # per-tile partials sit where the materialised path puts them
+    n, t = c["n"], c["tiles"]
+    part = (n * t * 4 + 255) // 256 * 256
+    pm = ws[256:256 + n * t * 4].view(torch.float32).view(n, t).double().cpu().numpy()
+    ps = ws[256 + part:256 + part + n * t * 4].view(torch.float32).view(n, t).double().cpu().numpy()
+    zp = np.full((n, c["v_pad"]), np.nan)  # padded columns never count
+    zp[:, :c["v_real"]] = z
+    om, os_ = o.tile_partials(zp, real_vocab=c["v_real"], padded_vocab=c["v_pad"], num_tiles=t)
+    ident = om == -np.inf
+    assert (pm[ident] == -np.inf).all() and (ps[ident] == 0.0).all()
+    assert np.max(np.abs(pm[~ident] - om[~ident])) <= 1e-4
+    rel = np.abs(ps[~ident] * np.exp(pm[~ident] - om[~ident]) - os_[~ident]) / os_[~ident]
+    assert rel.max() <= 1e-4, rel.max()
+    # the target logit is the fp32 accumulator: logp + LSE recovers z[target]
+    ztg = z[np.arange(n), np.where(act, t_h, 0)]
+    rec = logp.double().cpu().numpy() + lse.double().cpu().numpy()
+    assert np.max(np.abs(rec[act] - ztg[act])) <= 1e-4
+
+
+def test_fused_repeat_and_batch_invariance():
+    h, w, tgt, mask = make_case(300, 128, 2500, 2560, seed=3)
+    a = run(h, w, tgt, mask, 2500, 2560, 10)
+    b = run(h, w, tgt, mask, 2500, 2560, 10)
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+    for r in (0, 129, 299):  # a token's result does not depend on the batch
+        one = run(h[r:r + 1].contiguous(), w, tgt[r:r + 1], mask[r:r + 1], 2500, 2560, 10)
+        assert one[0].view(torch.int32)[0] == a[0].view(torch.int32)[r]
+        assert one[1].view(torch.int32)[0] == a[1].view(torch.int32)[r]
+
+
+def test_fused_validate_bad_target():
+    h, w, tgt, mask = make_case(40, 64, 1000, 1024, seed=5, mask_keep=1.1, ignore_frac=0.0)
+    tgt[7] = 1000  # a padded column is not a valid target
+    with pytest.raises(rlk.RlkError) as ei:
+        run(h, w, tgt, None, 1000, 1024, 4, validate=True)
+    assert ei.value.status == rlk.RLK_ERR_TARGET_RANGE
+    logp, _, _ = run(h, w, tgt, None, 1000, 1024, 4)
+    assert torch.isnan(logp[7]) and torch.isfinite(logp[torch.arange(40, device=DEV) != 7]).all()
+
+
+def test_fused_lmhead_4096_sampled():
+    """The LM-head workload: hidden [4096, 4096] ~ N(0,1), W [152576, 4096] ~ N(0, 0.02^2),
+    rows >= 151936 padding, 64 tiles, all tokens active; sampled tokens vs the oracle."""
+    n, k, v_real, v_pad = 4096, 4096, 151936, 152576
+    g = torch.Generator(device=DEV).manual_seed(123)
+    h = torch.randn((n, k), generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((v_pad, k), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    tgt = torch.randint(0, v_real, (n,), generator=g, device=DEV, dtype=torch.int32)
+    logp, lse, _ = run(h, w, tgt, None, v_real, v_pad, 64)
+    rows = np.array(sorted({0, 1, 255, 256, 2047, 4095} |
+                           set(np.random.default_rng(0).choice(n, 26, replace=False).tolist())))
+    o = oracle.get()
+    z = o.lmhead_logits(bf16_bits(h[torch.from_numpy(rows).to(DEV)]), bf16_bits(w),
+                        real_vocab=v_real)
+    t_h = tgt.cpu().numpy()[rows]
+    lo, so, _, _ = o.fwd(z, t_h, None, real_vocab=v_real)
+    stats = P.check_fwd(logp.cpu().numpy()[rows], lse.cpu().numpy()[rows], lo, so,
+                        np.ones(len(rows), bool), "lmhead 4096")
+    print(stats, flush=True)

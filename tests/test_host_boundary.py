@@ -207,3 +207,40 @@ def test_geometry_errors():
         with pytest.raises(rlk.RlkError) as ei:
             rlk.rlk_logp_tile_geometry(*args)
         assert ei.value.status == code
+
+
+def test_fused_lmhead_host_validation():
+    a = _FakeTensor(0x10000000)
+    s = _NoStream()
+    ok = desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=4)
+    need = rlk.rlk_logp_fused_lmhead_workspace_bytes(ok)
+    n_vb = (1000 + 255) // 256
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == 256 + 2 * r(8 * 4 * 4) + r(8 * 4) + 2 * r(8 * 2 * n_vb * 4)
+    ws = _FakeTensor(0x20000000, need)
+    cases = [
+        (desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=5), 64,
+         rlk.RLK_ERR_BAD_TILING),  # tiles narrower than 256 columns
+        (desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=4,
+              num_virtual_shards=2), 64, rlk.RLK_ERR_BAD_TILING),
+        (ok, 96, rlk.RLK_ERR_BAD_SHAPE),  # hidden_dim not a multiple of 64
+        (ok, 0, rlk.RLK_ERR_BAD_SHAPE),
+    ]
+    for d, k, code in cases:
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_fused_lmhead(d, a, a, k, a, None, a, a, ws, stream=s)
+        assert ei.value.status == code, (k, ei.value)
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_fused_lmhead(ok, a, a, 64, a, None, a, a, _FakeTensor(0x20000000, need - 1),
+                                  stream=s)
+    assert ei.value.status == rlk.RLK_ERR_WORKSPACE
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_fused_lmhead(ok, _FakeTensor(0x10000004), a, 64, a, None, a, a, ws, stream=s)
+    assert ei.value.status == rlk.RLK_ERR_ALIGNMENT
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.rlk_logp_fused_lmhead(ok, None, a, 64, a, None, a, a, ws, stream=s)
+    assert ei.value.status == rlk.RLK_ERR_NULL_POINTER
+    # an empty batch is a no-op
+    rlk.rlk_logp_fused_lmhead(desc(num_tokens=0, real_vocab=1000, padded_vocab=1024,
+                                   num_vocab_tiles=4), None, None, 64, None, None, None, None,
+                              None, stream=s)

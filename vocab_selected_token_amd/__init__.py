@@ -34,8 +34,9 @@ RLK_DTYPE_F32 = 0
 RLK_DTYPE_BF16 = 1
 RLK_FLAG_VALIDATE = 1
 
-EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd", "rlk_logp_tile_geometry",
-            "rlk_status_string", "rlk_last_error_detail")
+EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd",
+            "rlk_logp_fused_lmhead_workspace_bytes", "rlk_logp_fused_lmhead",
+            "rlk_logp_tile_geometry", "rlk_status_string", "rlk_last_error_detail")
 
 
 class rlk_logp_desc(ctypes.Structure):  # noqa: N801 - mirrors the C struct name
@@ -65,6 +66,10 @@ def _load() -> ctypes.CDLL:
     lib.rlk_logp_fwd.restype = ctypes.c_int
     lib.rlk_logp_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz, vp]
     lib.rlk_logp_bwd.restype = ctypes.c_int
+    lib.rlk_logp_fused_lmhead_workspace_bytes.argtypes = [dp]
+    lib.rlk_logp_fused_lmhead_workspace_bytes.restype = sz
+    lib.rlk_logp_fused_lmhead.argtypes = [dp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_fused_lmhead.restype = ctypes.c_int
     lib.rlk_logp_tile_geometry.argtypes = [i64, i32, i32, vp, vp]
     lib.rlk_logp_tile_geometry.restype = ctypes.c_int
     lib.rlk_status_string.argtypes = [ctypes.c_int]
@@ -117,6 +122,18 @@ def rlk_logp_bwd(desc, logits, targets, active_mask, lse, grad_logp, dlogits, ld
     _check(_lib.rlk_logp_bwd(ctypes.byref(desc), _ptr(logits), _ptr(targets), _ptr(active_mask),
                              _ptr(lse), _ptr(grad_logp), _ptr(dlogits), ld_dlogits,
                              dlogits_dtype, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_fused_lmhead_workspace_bytes(desc: rlk_logp_desc) -> int:
+    return int(_lib.rlk_logp_fused_lmhead_workspace_bytes(ctypes.byref(desc)))
+
+
+def rlk_logp_fused_lmhead(desc, hidden, weight, hidden_dim: int, targets, active_mask, logp, lse,
+                          workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_fused_lmhead(ctypes.byref(desc), _ptr(hidden), _ptr(weight), hidden_dim,
+                                      _ptr(targets), _ptr(active_mask), _ptr(logp), _ptr(lse),
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def rlk_logp_tile_geometry(padded_vocab: int, num_vocab_tiles: int, num_virtual_shards: int = 1):
@@ -187,3 +204,24 @@ def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torc
     rlk_logp_bwd(desc, logits, targets, _u8_mask(active_mask), lse, grad_logp, dl, ld_d, code,
                  workspace, stream)
     return dl[:, :v_pad]
+
+
+def fused_lmhead(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                 active_mask=None, *, real_vocab: int, padded_vocab: int | None = None,
+                 num_vocab_tiles: int = 64, ignore_index: int = -100, validate: bool = False,
+                 workspace: torch.Tensor | None = None, stream=None):
+    """(logp, lse) of z = hidden . weight^T without materialising z.
+    hidden: bf16 [N, K] contiguous; weight: bf16 [V_pad, K] contiguous."""
+    n, k = hidden.shape
+    v_pad = padded_vocab or weight.shape[0]
+    desc = make_desc(n, real_vocab, v_pad, v_pad, num_vocab_tiles, 1, ignore_index, validate)
+    logp = torch.empty(n, dtype=torch.float32, device=hidden.device)
+    lse = torch.empty(n, dtype=torch.float32, device=hidden.device)
+    if workspace is None:
+        nbytes = rlk_logp_fused_lmhead_workspace_bytes(desc)
+        if nbytes == 0:
+            raise ValueError(f"invalid rlk_logp_desc: {rlk_last_error_detail()}")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
+    rlk_logp_fused_lmhead(desc, hidden, weight, k, targets, _u8_mask(active_mask), logp, lse,
+                          workspace, stream)
+    return logp, lse

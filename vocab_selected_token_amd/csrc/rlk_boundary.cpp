@@ -187,6 +187,7 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
   }
   rlk::Stage2Args a2;
   a2.logits = logits;
+  a2.target_logit = nullptr;
   a2.ld = desc->ld_logits;
   a2.num_rows = (int32_t)n;
   a2.real_vocab = (int32_t)desc->real_vocab;
@@ -262,6 +263,140 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
   e = rlk::launch_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "bwd_dlogits launch");
   if (validate) return finish_validate(status, stream, false);
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Fused LM-head variant.
+// ---------------------------------------------------------------------------
+namespace {
+
+rlk_status check_fused_desc(const rlk_logp_desc* d) {
+  if (!d) return fail(RLK_ERR_NULL_POINTER, "desc is NULL");
+  if (d->num_tokens < 0 || d->num_tokens > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "num_tokens=%lld outside [0, 2^31-1]",
+                (long long)d->num_tokens);
+  if (d->real_vocab < 1 || d->padded_vocab < d->real_vocab || d->padded_vocab > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "need 1 <= real_vocab=%lld <= padded_vocab=%lld <= 2^31-1",
+                (long long)d->real_vocab, (long long)d->padded_vocab);
+  if (d->num_vocab_tiles < 1 || (int64_t)d->num_vocab_tiles > d->padded_vocab)
+    return fail(RLK_ERR_BAD_TILING, "num_vocab_tiles=%d outside [1, padded_vocab]",
+                d->num_vocab_tiles);
+  if (d->padded_vocab / d->num_vocab_tiles < rlk::kLmheadBlockVocab)
+    return fail(RLK_ERR_BAD_TILING,
+                "fused LM-head needs tiles of at least %d columns (padded_vocab / "
+                "num_vocab_tiles = %lld)",
+                rlk::kLmheadBlockVocab, (long long)(d->padded_vocab / d->num_vocab_tiles));
+  if (d->num_virtual_shards != 1)
+    return fail(RLK_ERR_BAD_TILING, "fused LM-head takes num_virtual_shards = 1 (got %d)",
+                d->num_virtual_shards);
+  if (d->flags & ~RLK_FLAG_VALIDATE)
+    return fail(RLK_ERR_BAD_SHAPE, "unknown flag bits 0x%x", d->flags & ~RLK_FLAG_VALIDATE);
+  return RLK_OK;
+}
+
+struct FusedLayout {
+  size_t pmax, psum, tlogit, seg_m, seg_s, total;
+};
+
+FusedLayout fused_layout(const rlk_logp_desc* d) {
+  const size_t n = (size_t)d->num_tokens;
+  const size_t n_vb = ((size_t)d->real_vocab + rlk::kLmheadBlockVocab - 1) /
+                      rlk::kLmheadBlockVocab;
+  const size_t part = round256(n * (size_t)d->num_vocab_tiles * sizeof(float));
+  const size_t seg = round256(n * 2 * n_vb * sizeof(float));
+  FusedLayout l;
+  l.pmax = kStatusBytes;
+  l.psum = l.pmax + part;
+  l.tlogit = l.psum + part;
+  l.seg_m = l.tlogit + round256(n * sizeof(float));
+  l.seg_s = l.seg_m + seg;
+  l.total = l.seg_s + seg;
+  return l;
+}
+
+}  // namespace
+
+size_t rlk_logp_fused_lmhead_workspace_bytes(const rlk_logp_desc* desc) {
+  if (check_fused_desc(desc) != RLK_OK) return 0;
+  return fused_layout(desc).total;
+}
+
+rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
+                                 const void* weight, int64_t hidden_dim, const int32_t* targets,
+                                 const uint8_t* active_mask, float* logp, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_fused_desc(desc);
+  if (st != RLK_OK) return st;
+  if (hidden_dim < rlk::kLmheadSlabK || hidden_dim % rlk::kLmheadSlabK != 0 ||
+      hidden_dim > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "hidden_dim=%lld must be a positive multiple of %d",
+                (long long)hidden_dim, rlk::kLmheadSlabK);
+  const int64_t n = desc->num_tokens;
+  if (n == 0) return ok();
+  if (!hidden || !weight || !targets || !logp || !lse)
+    return fail(RLK_ERR_NULL_POINTER, "hidden, weight, targets, logp and lse must be non-NULL");
+  const FusedLayout lay = fused_layout(desc);
+  if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < lay.total)
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes,
+                lay.total);
+  if (!aligned(hidden, 16) || !aligned(weight, 16))
+    return fail(RLK_ERR_ALIGNMENT, "hidden and weight must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, logp and lse must be 4-byte aligned");
+  // the kernel addresses both operands with 32-bit offsets in 16-byte chunks
+  if ((int64_t)desc->real_vocab * (hidden_dim / 8) > kI32Max || n * (hidden_dim / 8) > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "hidden or weight holds 2^31 or more 16-byte chunks");
+  if (rlk::lmhead_grid_blocks((int32_t)n, (int32_t)desc->real_vocab) > kI32Max)
+    return fail(RLK_ERR_BAD_SHAPE, "num_tokens x vocabulary blocks too large for one launch");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
+  hipError_t e;
+  if (validate) {
+    e = rlk::launch_clear_status(status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+  }
+  rlk::LmheadArgs a;
+  a.hidden = hidden;
+  a.weight = weight;
+  a.hidden_dim = (int32_t)hidden_dim;
+  a.num_tokens = (int32_t)n;
+  a.real_vocab = (int32_t)desc->real_vocab;
+  a.padded_vocab = (int32_t)desc->padded_vocab;
+  a.num_tiles = desc->num_vocab_tiles;
+  a.targets = targets;
+  a.mask = active_mask;
+  a.ignore_index = desc->ignore_index;
+  a.seg_m = reinterpret_cast<float*>(ws + lay.seg_m);
+  a.seg_s = reinterpret_cast<float*>(ws + lay.seg_s);
+  a.target_logit = reinterpret_cast<float*>(ws + lay.tlogit);
+  a.pmax = reinterpret_cast<float*>(ws + lay.pmax);
+  a.psum = reinterpret_cast<float*>(ws + lay.psum);
+  e = rlk::launch_lmhead(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "lmhead launch");
+  rlk::Stage2Args a2;
+  a2.logits = nullptr;
+  a2.target_logit = a.target_logit;
+  a2.ld = 0;
+  a2.num_rows = (int32_t)n;
+  a2.real_vocab = (int32_t)desc->real_vocab;
+  a2.num_tiles = desc->num_vocab_tiles;
+  a2.pmax = a.pmax;
+  a2.psum = a.psum;
+  a2.targets = targets;
+  a2.mask = active_mask;
+  a2.ignore_index = desc->ignore_index;
+  a2.logp = logp;
+  a2.lse = lse;
+  a2.status = status;
+  e = rlk::launch_stage2(a2, stream);
+  if (e != hipSuccess) return hip_fail(e, "stage2_merge launch");
+  if (validate) return finish_validate(status, stream, true);
   return ok();
 }
 

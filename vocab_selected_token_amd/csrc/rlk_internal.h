@@ -23,7 +23,8 @@ struct Stage1Args {
 };
 
 struct Stage2Args {
-  const void* logits;
+  const void* logits;           // bf16 logits for the target gather, or
+  const float* target_logit;    // if non-null: the fp32 target logit of each row
   int64_t ld;
   int32_t num_rows;
   int32_t real_vocab;
@@ -55,7 +56,32 @@ struct BwdArgs {
   uint32_t* status;
 };
 
+// Fused LM-head variant: vocabulary rows per GEMM block (tiles must be at
+// least this wide, so a block holds at most one tile bound).
+constexpr int32_t kLmheadBlockVocab = 256;
+constexpr int32_t kLmheadSlabK = 64;  // hidden_dim must be a multiple of this
+
+struct LmheadArgs {
+  const void* hidden;  // bf16 [num_tokens, hidden_dim]
+  const void* weight;  // bf16 [>= real_vocab, hidden_dim]
+  int32_t hidden_dim;
+  int32_t num_tokens;
+  int32_t real_vocab;
+  int32_t padded_vocab;
+  int32_t num_tiles;
+  const int32_t* targets;
+  const uint8_t* mask;  // may be null
+  int32_t ignore_index;
+  float* seg_m;  // [num_tokens][2 * ceil(real_vocab / 256)]
+  float* seg_s;
+  float* target_logit;  // [num_tokens]
+  float* pmax;          // [num_tokens][num_tiles]
+  float* psum;
+};
+
 int64_t stage1_blocks(int64_t items);
+int64_t lmhead_grid_blocks(int32_t num_tokens, int32_t real_vocab);
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
 int64_t bwd_col_blocks(int32_t padded_vocab);
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream);

@@ -308,7 +308,8 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
 }
 
 __global__ __launch_bounds__(kMergeThreads) void stage2_merge(
-    const uint16_t* __restrict__ logits, int64_t ld, int32_t num_rows, int32_t real_vocab,
+    const uint16_t* __restrict__ logits, const float* __restrict__ target_logit, int64_t ld,
+    int32_t num_rows, int32_t real_vocab,
     int32_t num_tiles, const float* __restrict__ pmax, const float* __restrict__ psum,
     const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
     float* __restrict__ logp, float* __restrict__ lse, uint32_t* __restrict__ status) {
@@ -329,7 +330,8 @@ __global__ __launch_bounds__(kMergeThreads) void stage2_merge(
     status[0] = 1u;
     return;
   }
-  const float x = __uint_as_float((uint32_t)logits[(int64_t)r * ld + tgt] << 16);
+  const float x = target_logit ? target_logit[r]
+                               : __uint_as_float((uint32_t)logits[(int64_t)r * ld + tgt] << 16);
   logp[r] = x - L;
   if (!__builtin_isfinite(L)) status[1] = 1u;
 }
@@ -474,7 +476,8 @@ hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((a.num_rows + kMergeThreads - 1) / kMergeThreads));
   hipLaunchKernelGGL(stage2_merge, grid, dim3(kMergeThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(a.logits), a.ld, a.num_rows, a.real_vocab,
+                     reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
+                     a.num_rows, a.real_vocab,
                      a.num_tiles, a.pmax, a.psum, a.targets, a.mask, a.ignore_index, a.logp,
                      a.lse, a.status);
   return hipGetLastError();

@@ -1,0 +1,383 @@
+// rlk_lmhead.hip -- fused LM-head variant for gfx950: selected-token logp of
+// z = h . W^T without writing the logits to memory.
+//
+// The pages name an optional fused kernel without describing it (Issue #323
+// "[WS2][Logprob] H100 validation and reproduction guide for Issue #241
+// PR1-PR5", "Validation Boundary": the optional PR6 fused kernel).  This file
+// keeps the contract of the materialised path (PR #289 "[WS2][PR4][Logp] feat:
+// add distributed TP/CP logprob drift report", PR1 commit messages: per-tile
+// fp32 (max, sumexp) over real columns, the (-inf, 0) identity, a merge in
+// fixed global tile order) and takes the statistics straight from the fp32
+// GEMM accumulators.
+//
+// Two kernels run before the ordinary stage-2 merge:
+//   lmhead_segments  bf16 MFMA GEMM of a 256-vocab x 256-token block over the
+//                    whole hidden dimension, then, per token, the (max, sumexp)
+//                    of each "segment" -- the part of the block's vocabulary
+//                    that lies in one tile (a block holds at most one tile
+//                    bound, since tiles are at least 256 columns wide) -- and
+//                    the fp32 target logit of every token whose target falls in
+//                    the block.
+//   lmhead_tiles     per (token, tile): merge the tile's segments in ascending
+//                    column order into the tile partial, in the same [N][T]
+//                    layout that stage 1 of the materialised path writes.
+//
+// GEMM layout.  The accumulator is C[vocab][token] = W . h^T: W rows are the
+// MFMA "A" operand and hidden rows the "B" operand, both K-contiguous.  With
+// v_mfma_f32_32x32x16_bf16, lane l supplies row/col l%32 and k in
+// [8*(l/32), 8*(l/32)+8); accumulator i of lane l is C[8*(i/4) + 4*(l/32) +
+// i%4][l%32].  So each lane holds 16 vocab rows of one token per 32x32 tile and
+// a token's reduction over the vocabulary stays mostly inside one lane.  The
+// 256 threads form 2 x 2 waves of 128 vocab x 128 tokens (4 x 4 MFMA tiles, 256
+// fp32 accumulators per lane).  K advances in slabs of 64 through
+// double-buffered LDS whose rows are padded from 128 to 144 bytes, so that the
+// 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+//
+// Determinism: every reduction has a fixed order -- each lane over its rows in
+// register order, then the lane pair (l, l+32), then the two vocab halves of
+// the block (the lower half first), then the segments of a tile in ascending
+// column order, then the tiles in stage 2.  No atomics.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_internal.h"
+
+namespace rlk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+constexpr int kThreads = 256;
+constexpr int kBV = 256;  // vocabulary rows per block (= kLmheadBlockVocab)
+constexpr int kBT = 256;  // tokens per block
+constexpr int kBK = 64;   // hidden-dimension slab per LDS stage
+constexpr int kRowBytes = kBK * 2 + 16;     // 144: padded LDS row
+constexpr int kSlabBytes = kBV * kRowBytes;  // one operand, one stage
+constexpr int kRowsPerPass = kThreads / 8;   // 32 rows per thread pass (8 chunks per row)
+constexpr int kCopies = kBV / kRowsPerPass;  // 8 chunks per operand per thread per slab
+
+static_assert(kBV == kLmheadBlockVocab, "block width shared with the boundary");
+static_assert(kBV == kBT, "the copy loop assumes square blocks");
+
+__device__ __forceinline__ float maxnan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int64_t xcd_local_block(int64_t b, int64_t nb) {
+  constexpr int64_t kXcds = 8;
+  const int64_t per = nb / kXcds, rem = nb % kXcds, x = b % kXcds, l = b / kXcds;
+  return x * per + (x < rem ? x : rem) + l;
+}
+
+// Column bound of the first tile boundary strictly inside [v0, v0 + kBV), or
+// v0 + kBV if there is none.  Tile t spans [floor(t*V/T), floor((t+1)*V/T)).
+__device__ __forceinline__ int32_t inner_tile_bound(int32_t v0, int32_t padded_vocab,
+                                                    int32_t num_tiles) {
+  // the tile holding column v0 is the largest t with floor(t*V/T) <= v0
+  const int64_t t = ((int64_t)(v0 + 1) * num_tiles - 1) / padded_vocab;
+  const int32_t b = (int32_t)(((t + 1) * padded_vocab) / num_tiles);
+  return (b > v0 && b < v0 + kBV) ? b : v0 + kBV;
+}
+
+// ---------------------------------------------------------------------------
+// lmhead_segments
+//   h          bf16 [num_tokens, K] (16-byte chunks, K/8 per row)
+//   w          bf16 [>= real_vocab, K]; rows >= real_vocab are never read
+//   seg_m/s    [num_tokens][2 * n_vb]: slot 2*vb holds the block's columns
+//              before its inner tile bound (all of them if there is none), slot
+//              2*vb+1 those from the bound on ((-inf, 0) if there is none)
+//   tlogit     [num_tokens] fp32 target logit, written for effective-active
+//              tokens whose target is a real column of this block
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void lmhead_segments(
+    const uint4* __restrict__ h, const uint4* __restrict__ w, int32_t hidden_dim,
+    int32_t num_tokens, int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles,
+    int32_t n_vb, int32_t n_tb, const int32_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ seg_m,
+    float* __restrict__ seg_s, float* __restrict__ tlogit) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kSlabBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave >> 1;  // vocabulary half of the block
+  const int wt = wave & 1;   // token half of the block
+
+  // blocks of one vocabulary slice (all token blocks) run on one XCD, so the
+  // slice of W they all read stays in that XCD's L2
+  const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
+  const int32_t vb = (int32_t)(blk / n_tb);
+  const int32_t tb = (int32_t)(blk - (int64_t)vb * n_tb);
+  const int32_t v0 = vb * kBV;
+  const int32_t t0 = tb * kBT;
+  const int32_t ldc = hidden_dim / 8;  // 16-byte chunks per row
+
+  // global -> LDS copy: thread tid moves chunk (tid & 7) of rows (tid >> 3) + 32j.
+  // Offsets are in 16-byte chunks from the operand base (the boundary checks
+  // that both operands hold fewer than 2^31 chunks).
+  const int kc = tid & 7;
+  const int r0 = tid >> 3;
+  int32_t woff[kCopies], hoff[kCopies];
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    const int32_t wr = min(v0 + r0 + kRowsPerPass * j, real_vocab - 1);  // clamp: never read padding
+    const int32_t hr = min(t0 + r0 + kRowsPerPass * j, num_tokens - 1);
+    woff[j] = wr * ldc + kc;
+    hoff[j] = hr * ldc + kc;
+  }
+  const int st_off = r0 * kRowBytes + kc * 16;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  uint4 sa[kCopies], sb[kCopies];
+  const int nslab = hidden_dim / kBK;
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    sa[j] = w[woff[j]];
+    sb[j] = h[hoff[j]];
+  }
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    *reinterpret_cast<uint4*>(smem + st_off + j * kRowsPerPass * kRowBytes) = sa[j];
+    *reinterpret_cast<uint4*>(smem + kSlabBytes + st_off + j * kRowsPerPass * kRowBytes) = sb[j];
+  }
+  __syncthreads();
+
+  // fragment read offsets (bytes) inside one operand stage
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 16;
+  for (int s = 0; s < nslab; ++s) {
+    // prefetch the next slab (the last iteration re-reads its own slab and
+    // stores it to the idle buffer, which nothing reads again)
+    const int32_t nxt = min(s + 1, nslab - 1) * (kBK / 8);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      sa[j] = w[woff[j] + nxt];
+      sb[j] = h[hoff[j] + nxt];
+    }
+    const char* As = smem + (s & 1) * 2 * kSlabBytes;
+    const char* Bs = As + kSlabBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+        af[vs] = *reinterpret_cast<const bf16x8*>(
+            As + (wv * 128 + vs * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);
+#pragma unroll
+      for (int ts = 0; ts < 4; ++ts)
+        bfr[ts] = *reinterpret_cast<const bf16x8*>(
+            Bs + (wt * 128 + ts * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts)
+          acc[vs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts],
+                                                                0, 0, 0);
+    }
+    char* Ad = smem + ((s + 1) & 1) * 2 * kSlabBytes;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      *reinterpret_cast<uint4*>(Ad + st_off + j * kRowsPerPass * kRowBytes) = sa[j];
+      *reinterpret_cast<uint4*>(Ad + kSlabBytes + st_off + j * kRowsPerPass * kRowBytes) = sb[j];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const int32_t bnd = inner_tile_bound(v0, padded_vocab, num_tiles);
+  const int32_t vw0 = v0 + wv * 128;            // first vocabulary row of this wave
+  const int32_t row_lane = 4 * (lane >> 5);     // lane-half offset inside an 8-row group
+  float* xch = reinterpret_cast<float*>(smem);  // [2 token halves][128 tokens][4]
+  // every row of the block is real and no tile bound cuts it: one segment, no masks
+  const bool simple = (v0 + kBV <= real_vocab) && (bnd == v0 + kBV);
+
+#pragma unroll
+  for (int ts = 0; ts < 4; ++ts) {
+    const int32_t tok = t0 + wt * 128 + ts * 32 + (lane & 31);
+    int32_t trow = -1;  // the target's column if this wave holds it
+    if (tok < num_tokens && (mask == nullptr || mask[tok] != 0)) {
+      const int32_t tg = targets[tok];
+      if (tg != ignore_index && tg >= vw0 && tg < vw0 + 128 && tg < real_vocab) trow = tg;
+    }
+    if (__any(trow >= 0)) {  // rare: some token of this wave has its target here
+      float tz = 0.0f;
+      bool have_t = false;
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+          if (row == trow) {
+            tz = acc[vs][ts][i];
+            have_t = true;
+          }
+        }
+      if (have_t) tlogit[tok] = tz;
+    }
+    float m0 = kNegInf, m1 = kNegInf, s0 = 0.0f, s1 = 0.0f;
+    if (simple) {
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m0 = maxnan(m0, acc[vs][ts][i]);
+      // the lane pair (l, l+32) holds the other rows of the same token
+      m0 = maxnan(m0, __shfl_xor(m0, 32));
+      const float b0 = (m0 == kNegInf) ? 0.0f : m0;
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
+    } else {
+      // pass 1: per-segment maxima over this lane's real rows
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+          const float z = acc[vs][ts][i];
+          if (row < real_vocab && row < bnd) m0 = maxnan(m0, z);
+          if (row < real_vocab && row >= bnd) m1 = maxnan(m1, z);
+        }
+      m0 = maxnan(m0, __shfl_xor(m0, 32));
+      m1 = maxnan(m1, __shfl_xor(m1, 32));
+      // pass 2: sums of exp(z - max) relative to the pair maxima
+      const float b0 = (m0 == kNegInf) ? 0.0f : m0;
+      const float b1 = (m1 == kNegInf) ? 0.0f : m1;
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+          const float z = (row < real_vocab) ? acc[vs][ts][i] : kNegInf;
+          const bool hi = row >= bnd;
+          const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
+          s0 += hi ? 0.0f : e;
+          s1 += hi ? e : 0.0f;
+        }
+    }
+    // lane pair: the same two addends in both lanes, so both hold the same sum
+    const float p0 = __shfl_xor(s0, 32), p1 = __shfl_xor(s1, 32);
+    s0 = (lane < 32) ? s0 + p0 : p0 + s0;
+    s1 = (lane < 32) ? s1 + p1 : p1 + s1;
+    if (wv == 1 && lane < 32) {
+      float* x = xch + ((wt * 128 + ts * 32 + lane) * 4);
+      x[0] = m0;
+      x[1] = s0;
+      x[2] = m1;
+      x[3] = s1;
+    }
+    // keep this token's values in registers of the lower-half wave
+    if (wv == 0) {
+      acc[0][ts][0] = m0;
+      acc[0][ts][1] = s0;
+      acc[0][ts][2] = m1;
+      acc[0][ts][3] = s1;
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && lane < 32) {
+    const int64_t seg_ld = 2 * (int64_t)n_vb;
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+      const int32_t tok = t0 + wt * 128 + ts * 32 + lane;
+      if (tok >= num_tokens) continue;
+      const float* x = xch + ((wt * 128 + ts * 32 + lane) * 4);
+      float out_m[2], out_s[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        // lower vocabulary half first, then the upper half
+        const float ma = acc[0][ts][2 * g], sa_ = acc[0][ts][2 * g + 1];
+        const float mb = x[2 * g], sb_ = x[2 * g + 1];
+        const float M = maxnan(ma, mb);
+        float S = 0.0f;
+        if (M != kNegInf) {
+          if (ma != kNegInf) S = sa_ * exp2_hw((ma - M) * kLog2e);
+          if (mb != kNegInf) S = fmaf(sb_, exp2_hw((mb - M) * kLog2e), S);
+        }
+        out_m[g] = M;
+        out_s[g] = S;
+      }
+      float* om = seg_m + (int64_t)tok * seg_ld + 2 * vb;
+      float* os = seg_s + (int64_t)tok * seg_ld + 2 * vb;
+      om[0] = out_m[0];
+      om[1] = out_m[1];
+      os[0] = out_s[0];
+      os[1] = out_s[1];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// lmhead_tiles: one thread per (token, tile); segments in ascending columns.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lmhead_tiles(
+    const float* __restrict__ seg_m, const float* __restrict__ seg_s, int32_t num_tokens,
+    int32_t n_vb, int32_t padded_vocab, int32_t num_tiles, float* __restrict__ pmax,
+    float* __restrict__ psum) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)num_tokens * num_tiles) return;
+  const int32_t tok = (int32_t)(idx / num_tiles);
+  const int32_t t = (int32_t)(idx - (int64_t)tok * num_tiles);
+  const int32_t c0 = (int32_t)(((int64_t)t * padded_vocab) / num_tiles);
+  const int32_t c1 = (int32_t)(((int64_t)(t + 1) * padded_vocab) / num_tiles);
+  const int32_t vb_first = c0 / kBV;
+  const int32_t vb_last = min((c1 - 1) / kBV, n_vb - 1);
+  const int64_t seg_ld = 2 * (int64_t)n_vb;
+  float M = kNegInf, S = 0.0f;
+  for (int32_t vb = vb_first; vb <= vb_last; ++vb) {
+    const int slot = (vb == vb_first && c0 > vb * kBV) ? 1 : 0;
+    const float m = seg_m[(int64_t)tok * seg_ld + 2 * vb + slot];
+    const float s = seg_s[(int64_t)tok * seg_ld + 2 * vb + slot];
+    if (m == kNegInf) continue;  // identity segment
+    if (M == kNegInf) {
+      M = m;
+      S = s;
+      continue;
+    }
+    const float nm = maxnan(M, m);
+    S = fmaf(s, exp2_hw((m - nm) * kLog2e), S * exp2_hw((M - nm) * kLog2e));
+    M = nm;
+  }
+  pmax[idx] = M;
+  psum[idx] = (M == kNegInf) ? 0.0f : S;
+}
+
+}  // namespace
+
+int64_t lmhead_grid_blocks(int32_t num_tokens, int32_t real_vocab) {
+  const int64_t n_vb = ((int64_t)real_vocab + kBV - 1) / kBV;
+  const int64_t n_tb = ((int64_t)num_tokens + kBT - 1) / kBT;
+  return n_vb * n_tb;
+}
+
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int32_t n_vb = (a.real_vocab + kBV - 1) / kBV;
+  const int32_t n_tb = (a.num_tokens + kBT - 1) / kBT;
+  hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)((int64_t)n_vb * n_tb)), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(a.hidden),
+                     reinterpret_cast<const uint4*>(a.weight), a.hidden_dim, a.num_tokens,
+                     a.real_vocab, a.padded_vocab, a.num_tiles, n_vb, n_tb, a.targets, a.mask,
+                     a.ignore_index, a.seg_m, a.seg_s, a.target_logit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)a.num_tokens * a.num_tiles;
+  hipLaunchKernelGGL(lmhead_tiles, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
+                     a.seg_m, a.seg_s, a.num_tokens, n_vb, a.padded_vocab, a.num_tiles, a.pmax,
+                     a.psum);
+  return hipGetLastError();
+}
+
+}  // namespace rlk
