@@ -28,10 +28,12 @@
 // [8*(l/32), 8*(l/32)+8); accumulator i of lane l is C[8*(i/4) + 4*(l/32) +
 // i%4][l%32].  So each lane holds 16 vocab rows of one token per 32x32 tile and
 // a token's reduction over the vocabulary stays mostly inside one lane.  The
-// 256 threads form 2 x 2 waves of 128 vocab x 128 tokens (4 x 4 MFMA tiles, 256
-// fp32 accumulators per lane).  K advances in slabs of 64 through
-// double-buffered LDS whose rows are padded from 128 to 144 bytes, so that the
-// 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+// 512 threads form 2 x 4 waves of 128 vocab x 64 tokens (4 x 2 MFMA tiles, 128
+// fp32 accumulators per lane), two waves per SIMD, so one wave's MFMAs run while
+// the other waits on memory.  K advances in slabs of 64 through double-buffered
+// LDS whose rows are padded from 128 to 144 bytes, so that the 16-byte fragment
+// reads of 8 consecutive lanes hit distinct banks; two register staging sets
+// keep the global loads of the next two slabs in flight.
 //
 // Determinism: every reduction has a fixed order -- each lane over its rows in
 // register order, then the lane pair (l, l+32), then the two vocab halves of
@@ -47,20 +49,28 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector: arrays of it stay in registers (HIP's uint4 is
+// a struct around a union, which keeps arrays of it in scratch memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kBV = 256;  // vocabulary rows per block (= kLmheadBlockVocab)
 constexpr int kBT = 256;  // tokens per block
 constexpr int kBK = 64;   // hidden-dimension slab per LDS stage
 constexpr int kRowBytes = kBK * 2 + 16;     // 144: padded LDS row
 constexpr int kSlabBytes = kBV * kRowBytes;  // one operand, one stage
-constexpr int kRowsPerPass = kThreads / 8;   // 32 rows per thread pass (8 chunks per row)
-constexpr int kCopies = kBV / kRowsPerPass;  // 8 chunks per operand per thread per slab
+constexpr int kRowsPerPass = kThreads / 8;   // 64 rows per thread pass (8 chunks per row)
+constexpr int kCopies = kBV / kRowsPerPass;  // 4 chunks per operand per thread per slab
 
 static_assert(kBV == kLmheadBlockVocab, "block width shared with the boundary");
+static_assert(kCopies == 4, "RLK_FOR4 spells out the four copies");
+
+// Spell a 4-way loop out with literal indices, so the staging arrays are
+// promoted to registers before any loop unrolling happens.
+#define RLK_FOR4(M) M(0) M(1) M(2) M(3)
 static_assert(kBV == kBT, "the copy loop assumes square blocks");
 
 __device__ __forceinline__ float maxnan(float a, float b) {
@@ -95,7 +105,7 @@ __device__ __forceinline__ int32_t inner_tile_bound(int32_t v0, int32_t padded_v
 //              tokens whose target is a real column of this block
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void lmhead_segments(
-    const uint4* __restrict__ h, const uint4* __restrict__ w, int32_t hidden_dim,
+    const u32x4* __restrict__ h, const u32x4* __restrict__ w, int32_t hidden_dim,
     int32_t num_tokens, int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles,
     int32_t n_vb, int32_t n_tb, const int32_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ seg_m,
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wv = wave >> 1;  // vocabulary half of the block
-  const int wt = wave & 1;   // token half of the block
+  const int wv = wave >> 2;  // vocabulary half of the block
+  const int wt = wave & 3;   // token quarter of the block
 
   // blocks of one vocabulary slice (all token blocks) run on one XCD, so the
   // slice of W they all read stays in that XCD's L2
@@ -117,95 +127,111 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int32_t t0 = tb * kBT;
   const int32_t ldc = hidden_dim / 8;  // 16-byte chunks per row
 
-  // global -> LDS copy: thread tid moves chunk (tid & 7) of rows (tid >> 3) + 32j.
+  // global -> LDS copy: thread tid moves chunk (tid & 7) of rows (tid >> 3) + 64j.
   // Offsets are in 16-byte chunks from the operand base (the boundary checks
   // that both operands hold fewer than 2^31 chunks).
   const int kc = tid & 7;
   const int r0 = tid >> 3;
   int32_t woff[kCopies], hoff[kCopies];
-#pragma unroll
-  for (int j = 0; j < kCopies; ++j) {
-    const int32_t wr = min(v0 + r0 + kRowsPerPass * j, real_vocab - 1);  // clamp: never read padding
-    const int32_t hr = min(t0 + r0 + kRowsPerPass * j, num_tokens - 1);
-    woff[j] = wr * ldc + kc;
-    hoff[j] = hr * ldc + kc;
-  }
+  // row clamps: padding rows of W and rows past the last token are never read
+#define RLK_OFFSETS(J)                                                                  \
+  woff[J] = min(v0 + r0 + kRowsPerPass * (J), real_vocab - 1) * ldc + kc;               \
+  hoff[J] = min(t0 + r0 + kRowsPerPass * (J), num_tokens - 1) * ldc + kc;
+  RLK_FOR4(RLK_OFFSETS)
+#undef RLK_OFFSETS
   const int st_off = r0 * kRowBytes + kc * 16;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  uint4 sa[kCopies], sb[kCopies];
+  // Two register staging sets give the global loads two slabs of MFMA work
+  // to arrive in: while slab s is multiplied out of LDS, slab s+1 waits in
+  // registers and slab s+2 is being fetched.
+  u32x4 sa0[kCopies], sb0[kCopies], sa1[kCopies], sb1[kCopies];
   const int nslab = hidden_dim / kBK;
-#pragma unroll
-  for (int j = 0; j < kCopies; ++j) {
-    sa[j] = w[woff[j]];
-    sb[j] = h[hoff[j]];
-  }
-#pragma unroll
-  for (int j = 0; j < kCopies; ++j) {
-    *reinterpret_cast<uint4*>(smem + st_off + j * kRowsPerPass * kRowBytes) = sa[j];
-    *reinterpret_cast<uint4*>(smem + kSlabBytes + st_off + j * kRowsPerPass * kRowBytes) = sb[j];
-  }
+  const int32_t last = (nslab - 1) * (kBK / 8);
+  const int32_t second = min(kBK / 8, last);
+#define RLK_PROLOGUE_LOAD(J)        \
+  sa0[J] = w[woff[J]];              \
+  sb0[J] = h[hoff[J]];              \
+  sa1[J] = w[woff[J] + second];     \
+  sb1[J] = h[hoff[J] + second];
+  RLK_FOR4(RLK_PROLOGUE_LOAD)
+#undef RLK_PROLOGUE_LOAD
+#define RLK_PROLOGUE_STORE(J)                                                              \
+  *reinterpret_cast<u32x4*>(smem + st_off + (J) * kRowsPerPass * kRowBytes) = sa0[J];      \
+  *reinterpret_cast<u32x4*>(smem + kSlabBytes + st_off + (J) * kRowsPerPass * kRowBytes) = \
+      sb0[J];
+  RLK_FOR4(RLK_PROLOGUE_STORE)
+#undef RLK_PROLOGUE_STORE
   __syncthreads();
 
   // fragment read offsets (bytes) inside one operand stage
   const int frag_row = lane & 31;
   const int frag_k = (lane >> 5) * 16;
-  for (int s = 0; s < nslab; ++s) {
-    // prefetch the next slab (the last iteration re-reads its own slab and
-    // stores it to the idle buffer, which nothing reads again)
-    const int32_t nxt = min(s + 1, nslab - 1) * (kBK / 8);
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) {
-      sa[j] = w[woff[j] + nxt];
-      sb[j] = h[hoff[j] + nxt];
-    }
-    const char* As = smem + (s & 1) * 2 * kSlabBytes;
-    const char* Bs = As + kSlabBytes;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
-        af[vs] = *reinterpret_cast<const bf16x8*>(
-            As + (wv * 128 + vs * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);
-#pragma unroll
-      for (int ts = 0; ts < 4; ++ts)
-        bfr[ts] = *reinterpret_cast<const bf16x8*>(
-            Bs + (wt * 128 + ts * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);
-#pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
-#pragma unroll
-        for (int ts = 0; ts < 4; ++ts)
-          acc[vs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts],
-                                                                0, 0, 0);
-    }
-    char* Ad = smem + ((s + 1) & 1) * 2 * kSlabBytes;
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) {
-      *reinterpret_cast<uint4*>(Ad + st_off + j * kRowsPerPass * kRowBytes) = sa[j];
-      *reinterpret_cast<uint4*>(Ad + kSlabBytes + st_off + j * kRowsPerPass * kRowBytes) = sb[j];
-    }
-    __syncthreads();
+
+// One slab: fetch slab S+2 into LD_A/LD_B, multiply slab S out of LDS stage
+// S&1, then store slab S+1 from ST_A/ST_B into the other stage.  Slab indices
+// past the end are clamped to the last slab; those loads and stores are never
+// consumed.  (A macro rather than a lambda keeps every array in registers.)
+#define RLK_LMHEAD_SLAB_STEP(S, LD_A, LD_B, ST_A, ST_B)                                       \
+  do {                                                                                      \
+    const int32_t nxt_ = min(((S) + 2) * (kBK / 8), last);                                  \
+    LD_A[0] = w[woff[0] + nxt_]; LD_B[0] = h[hoff[0] + nxt_];                               \
+    LD_A[1] = w[woff[1] + nxt_]; LD_B[1] = h[hoff[1] + nxt_];                               \
+    LD_A[2] = w[woff[2] + nxt_]; LD_B[2] = h[hoff[2] + nxt_];                               \
+    LD_A[3] = w[woff[3] + nxt_]; LD_B[3] = h[hoff[3] + nxt_];                               \
+    const char* As_ = smem + ((S) & 1) * 2 * kSlabBytes;                                    \
+    const char* Bs_ = As_ + kSlabBytes;                                                     \
+    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                               \
+      bf16x8 af[4], bfr[2];                                                                 \
+      _Pragma("unroll") for (int vs = 0; vs < 4; ++vs) af[vs] =                             \
+          *reinterpret_cast<const bf16x8*>(                                                 \
+              As_ + (wv * 128 + vs * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);        \
+      _Pragma("unroll") for (int ts = 0; ts < 2; ++ts) bfr[ts] =                            \
+          *reinterpret_cast<const bf16x8*>(                                                 \
+              Bs_ + (wt * 64 + ts * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);        \
+      _Pragma("unroll") for (int vs = 0; vs < 4; ++vs)                                      \
+          _Pragma("unroll") for (int ts = 0; ts < 2; ++ts) acc[vs][ts] =                    \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts], 0, 0, 0); \
+    }                                                                                       \
+    char* Ad_ = smem + (((S) + 1) & 1) * 2 * kSlabBytes + st_off;                           \
+    constexpr int kStep_ = kRowsPerPass * kRowBytes;                                        \
+    *reinterpret_cast<u32x4*>(Ad_ + 0 * kStep_) = ST_A[0];                                  \
+    *reinterpret_cast<u32x4*>(Ad_ + 1 * kStep_) = ST_A[1];                                  \
+    *reinterpret_cast<u32x4*>(Ad_ + 2 * kStep_) = ST_A[2];                                  \
+    *reinterpret_cast<u32x4*>(Ad_ + 3 * kStep_) = ST_A[3];                                  \
+    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 0 * kStep_) = ST_B[0];                     \
+    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 1 * kStep_) = ST_B[1];                     \
+    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 2 * kStep_) = ST_B[2];                     \
+    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 3 * kStep_) = ST_B[3];                     \
+    __syncthreads();                                                                        \
+  } while (0)
+
+  int s = 0;
+  for (; s + 1 < nslab; s += 2) {
+    RLK_LMHEAD_SLAB_STEP(s, sa0, sb0, sa1, sb1);      // slab s+2 -> set 0, s+1 from set 1
+    RLK_LMHEAD_SLAB_STEP(s + 1, sa1, sb1, sa0, sb0);  // slab s+3 -> set 1, s+2 from set 0
   }
+  if (s < nslab) RLK_LMHEAD_SLAB_STEP(s, sa0, sb0, sa1, sb1);
+#undef RLK_LMHEAD_SLAB_STEP
 
   // ---- epilogue -------------------------------------------------------------
   const int32_t bnd = inner_tile_bound(v0, padded_vocab, num_tiles);
   const int32_t vw0 = v0 + wv * 128;            // first vocabulary row of this wave
   const int32_t row_lane = 4 * (lane >> 5);     // lane-half offset inside an 8-row group
-  float* xch = reinterpret_cast<float*>(smem);  // [2 token halves][128 tokens][4]
+  float* xch = reinterpret_cast<float*>(smem);  // [256 tokens][4]
   // every row of the block is real and no tile bound cuts it: one segment, no masks
   const bool simple = (v0 + kBV <= real_vocab) && (bnd == v0 + kBV);
 
 #pragma unroll
-  for (int ts = 0; ts < 4; ++ts) {
-    const int32_t tok = t0 + wt * 128 + ts * 32 + (lane & 31);
+  for (int ts = 0; ts < 2; ++ts) {
+    const int32_t tok = t0 + wt * 64 + ts * 32 + (lane & 31);
     int32_t trow = -1;  // the target's column if this wave holds it
     if (tok < num_tokens && (mask == nullptr || mask[tok] != 0)) {
       const int32_t tg = targets[tok];
@@ -252,7 +278,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
         }
       m0 = maxnan(m0, __shfl_xor(m0, 32));
       m1 = maxnan(m1, __shfl_xor(m1, 32));
-      // pass 2: sums of exp(z - max) relative to the pair maxima
+      // pass 2: sums of exp(z - max) relative to the pair maxima.  The two
+      // thresholds go through an empty asm so the compiler recomputes the row
+      // tests here instead of keeping 128 masks alive from pass 1.
+      int32_t rv = real_vocab, bd = bnd;
+      asm volatile("" : "+s"(rv), "+s"(bd));
       const float b0 = (m0 == kNegInf) ? 0.0f : m0;
       const float b1 = (m1 == kNegInf) ? 0.0f : m1;
 #pragma unroll
@@ -260,8 +290,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
-          const float z = (row < real_vocab) ? acc[vs][ts][i] : kNegInf;
-          const bool hi = row >= bnd;
+          const float z = (row < rv) ? acc[vs][ts][i] : kNegInf;
+          const bool hi = row >= bd;
           const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
           s0 += hi ? 0.0f : e;
           s1 += hi ? e : 0.0f;
@@ -272,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     s0 = (lane < 32) ? s0 + p0 : p0 + s0;
     s1 = (lane < 32) ? s1 + p1 : p1 + s1;
     if (wv == 1 && lane < 32) {
-      float* x = xch + ((wt * 128 + ts * 32 + lane) * 4);
+      float* x = xch + ((wt * 64 + ts * 32 + lane) * 4);
       x[0] = m0;
       x[1] = s0;
       x[2] = m1;
@@ -290,10 +320,10 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   if (wv == 0 && lane < 32) {
     const int64_t seg_ld = 2 * (int64_t)n_vb;
 #pragma unroll
-    for (int ts = 0; ts < 4; ++ts) {
-      const int32_t tok = t0 + wt * 128 + ts * 32 + lane;
+    for (int ts = 0; ts < 2; ++ts) {
+      const int32_t tok = t0 + wt * 64 + ts * 32 + lane;
       if (tok >= num_tokens) continue;
-      const float* x = xch + ((wt * 128 + ts * 32 + lane) * 4);
+      const float* x = xch + ((wt * 64 + ts * 32 + lane) * 4);
       float out_m[2], out_s[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -367,8 +397,8 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream) {
   const int32_t n_vb = (a.real_vocab + kBV - 1) / kBV;
   const int32_t n_tb = (a.num_tokens + kBT - 1) / kBT;
   hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)((int64_t)n_vb * n_tb)), dim3(kThreads), 0,
-                     stream, reinterpret_cast<const uint4*>(a.hidden),
-                     reinterpret_cast<const uint4*>(a.weight), a.hidden_dim, a.num_tokens,
+                     stream, reinterpret_cast<const u32x4*>(a.hidden),
+                     reinterpret_cast<const u32x4*>(a.weight), a.hidden_dim, a.num_tokens,
                      a.real_vocab, a.padded_vocab, a.num_tiles, n_vb, n_tb, a.targets, a.mask,
                      a.ignore_index, a.seg_m, a.seg_s, a.target_logit);
   hipError_t e = hipGetLastError();
