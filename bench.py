@@ -109,6 +109,76 @@ def cpu_baseline(inp, wl, max_seconds: float) -> dict:
             "tokens_per_s": round(done_rows / elapsed, 2)}
 
 
+LMHEAD_WORKLOAD = "lmhead_b4096_k4096_v151936_p152576"
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, vendor figure
+
+
+def bench_lmhead(args) -> int:
+    """The fused LM-head variant: hidden [4096, 4096] ~ N(0,1), W [152576, 4096] ~ N(0, 0.02^2),
+    rows >= 151936 padding, 64 tiles, all tokens active, forward only."""
+    import torch
+
+    import vocab_selected_token_amd as rlk
+
+    dev = torch.device("cuda", 0)
+    n, k, v_real, v_pad, tiles = 4096, 4096, 151936, 152576, 64
+    g = torch.Generator(device=dev).manual_seed(123)
+    h = torch.randn((n, k), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((v_pad, k), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    tgt = torch.randint(0, v_real, (n,), generator=g, device=dev, dtype=torch.int32)
+    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, 1, -100)
+    ws = torch.empty(rlk.rlk_logp_fused_lmhead_workspace_bytes(desc), dtype=torch.uint8,
+                     device=dev)
+    logp = torch.empty(n, device=dev)
+    lse = torch.empty(n, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        rlk.rlk_logp_fused_lmhead(desc, h, w, k, tgt, None, logp, lse, ws, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        rlk.rlk_logp_fused_lmhead(desc, h, w, k, tgt, None, logp, lse, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * n * v_real * k  # padding rows are not computed
+    tflops = flops / (ev_ms * 1e-3) / 1e12
+    library = None
+    if args.library_gemm:  # context only: the plain library GEMM h . W^T of the same shape
+        wr = w[:v_real]
+        for _ in range(2):
+            torch.matmul(h, wr.t())
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            torch.matmul(h, wr.t())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lib_ms = e0.elapsed_time(e1) / args.steps
+        library = {"ms": round(lib_ms, 4), "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
+                   "note": "torch.matmul bf16 -> bf16 logits (materialised), no logp"}
+    line = {
+        "metric": "fused LM-head selected-token logp, TFLOP/s (MFMA utilisation)",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": LMHEAD_WORKLOAD, "tokens": n, "hidden": k, "real_vocab": v_real,
+                   "padded_vocab": v_pad, "vocab_tiles": tiles},
+        "tokens_per_s": round(n / (ev_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "lmhead_segments+lmhead_tiles+stage2_merge"},
+        "cpu_baseline": None,
+        "library_gemm": library,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +188,8 @@ def main() -> int:
     ap.add_argument("--shards", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="LM-head workload: also time the library GEMM of the same shape")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run an untimed plain copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -125,6 +197,9 @@ def main() -> int:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-device by design", file=sys.stderr)
         return 2
+
+    if args.workload == LMHEAD_WORKLOAD:
+        return bench_lmhead(args)
 
     import torch
 

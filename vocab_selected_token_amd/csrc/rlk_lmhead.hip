@@ -118,11 +118,20 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int wv = wave >> 2;  // vocabulary half of the block
   const int wt = wave & 3;   // token quarter of the block
 
-  // blocks of one vocabulary slice (all token blocks) run on one XCD, so the
-  // slice of W they all read stays in that XCD's L2
+  // Block order for L2 reuse.  Consecutive work indices land on one XCD (the
+  // XCD-local renumbering), and 32 consecutive indices -- one XCD's worth of
+  // resident blocks -- cover kGroupV vocabulary blocks x 8 token blocks: work
+  // index l sits in strip l / (kGroupV * n_tb) of kGroupV vocabulary blocks,
+  // token-block major inside the strip.  So each W slice is read by 8 resident
+  // blocks and each hidden slice by kGroupV, instead of every vocabulary block
+  // re-streaming all hidden states.
+  constexpr int32_t kGroupV = 4;
   const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
-  const int32_t vb = (int32_t)(blk / n_tb);
-  const int32_t tb = (int32_t)(blk - (int64_t)vb * n_tb);
+  const int64_t strip = blk / ((int64_t)kGroupV * n_tb);
+  const int32_t r_in = (int32_t)(blk - strip * kGroupV * n_tb);
+  const int32_t strip_w = min(kGroupV, n_vb - (int32_t)strip * kGroupV);  // last strip may be narrow
+  const int32_t vb = (int32_t)strip * kGroupV + r_in % strip_w;
+  const int32_t tb = r_in / strip_w;
   const int32_t v0 = vb * kBV;
   const int32_t t0 = tb * kBT;
   const int32_t ldc = hidden_dim / 8;  // 16-byte chunks per row
