@@ -51,6 +51,14 @@ def algorithmic_bytes(wl, n_active: int) -> dict:
     return {"fwd": fwd, "bwd": bwd}
 
 
+def algorithmic_bytes_one_pass(wl) -> int:
+    """Bytes the one-launch forward+backward must move: every real logit once,
+    every [N, V_pad] dlogit written, per row target 4, mask 1, g 4, logp 4, LSE 4."""
+    n = wl.num_tokens
+    out_b = 2 if wl.dlogits_dtype == "bf16" else 4
+    return n * wl.real_vocab * 2 + n * wl.padded_vocab * out_b + 17 * n
+
+
 def kernel_source_sha() -> str:
     """Hash of the kernel source with comments and whitespace removed: it changes
     exactly when the code the counters were taken on changes."""
@@ -188,6 +196,9 @@ def main() -> int:
     ap.add_argument("--shards", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-pass", action="store_true",
+                    help="time rlk_logp_fwd_bwd (g known before the forward) instead of "
+                         "rlk_logp_fwd + rlk_logp_bwd")
     ap.add_argument("--library-gemm", action="store_true",
                     help="LM-head workload: also time the library GEMM of the same shape")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -234,10 +245,22 @@ def main() -> int:
     masks = [b.mask.view(torch.uint8) for b in inps]
     stream = torch.cuda.current_stream()
 
+    one_pass = args.one_pass
+    if one_pass and not wl.backward:
+        log("bench: --one-pass needs a forward+backward workload")
+        return 2
+
     def step(i, events=None):
         b, m = inps[i % 2], masks[i % 2]
         if events:
             events[0].record(stream)
+        if one_pass:
+            rlk.rlk_logp_fwd_bwd(desc, b.logits, b.targets, m, b.grad, logp, lse, dl, ld_d, code,
+                                 ws, stream)
+            if events:
+                events[1].record(stream)
+                events[2].record(stream)
+            return
         rlk.rlk_logp_fwd(desc, b.logits, b.targets, m, logp, lse, ws, stream)
         if events:
             events[1].record(stream)
@@ -271,21 +294,33 @@ def main() -> int:
         log(f"bench: copy probe {nbytes} bytes x3 done")
         del src, dst
 
-    total_bytes = nb["fwd"] + (nb["bwd"] if wl.backward else 0)
-    value = total_bytes / (ms_step * 1e-3) / 1e9
-    fwd_gbs = nb["fwd"] / (fwd_ms * 1e-3) / 1e9
-    kernels = {"stage1_partials+stage2_merge": {"ms": round(fwd_ms, 4), "GB/s": round(fwd_gbs, 1),
-                                                "bytes": nb["fwd"]}}
-    if wl.backward:
-        bwd_gbs = nb["bwd"] / (bwd_ms * 1e-3) / 1e9
-        kernels["bwd_dlogits"] = {"ms": round(bwd_ms, 4), "GB/s": round(bwd_gbs, 1),
-                                  "bytes": nb["bwd"]}
-    dom = "bwd_dlogits" if wl.backward and bwd_ms >= fwd_ms else "stage1_partials+stage2_merge"
-    dom_gbs = kernels[dom]["GB/s"]
-    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic("bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
-                "kernel": dom}
+    if one_pass:
+        total_bytes = algorithmic_bytes_one_pass(wl)
+        value = total_bytes / (ms_step * 1e-3) / 1e9
+        k_gbs = total_bytes / (fwd_ms * 1e-3) / 1e9
+        kernels = {"fwd_bwd_rows": {"ms": round(fwd_ms, 4), "GB/s": round(k_gbs, 1),
+                                    "bytes": total_bytes}}
+        roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic("fwd_bwd_rows"), "kernel": "fwd_bwd_rows"}
+    else:
+        total_bytes = nb["fwd"] + (nb["bwd"] if wl.backward else 0)
+        value = total_bytes / (ms_step * 1e-3) / 1e9
+        fwd_gbs = nb["fwd"] / (fwd_ms * 1e-3) / 1e9
+        kernels = {"stage1_partials+stage2_merge": {"ms": round(fwd_ms, 4),
+                                                    "GB/s": round(fwd_gbs, 1),
+                                                    "bytes": nb["fwd"]}}
+        if wl.backward:
+            bwd_gbs = nb["bwd"] / (bwd_ms * 1e-3) / 1e9
+            kernels["bwd_dlogits"] = {"ms": round(bwd_ms, 4), "GB/s": round(bwd_gbs, 1),
+                                      "bytes": nb["bwd"]}
+        dom = ("bwd_dlogits" if wl.backward and bwd_ms >= fwd_ms
+               else "stage1_partials+stage2_merge")
+        dom_gbs = kernels[dom]["GB/s"]
+        roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic("bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
+                    "kernel": dom}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -300,7 +335,9 @@ def main() -> int:
         "config": {"workload": wl.name, "tokens": n, "active_tokens": n_active,
                    "real_vocab": wl.real_vocab, "padded_vocab": wl.padded_vocab,
                    "vocab_tiles": wl.num_tiles, "virtual_shards": args.shards,
-                   "dlogits_dtype": wl.dlogits_dtype, "parallelism": "single-gpu"},
+                   "dlogits_dtype": wl.dlogits_dtype, "parallelism": "single-gpu",
+                   "schedule": "one launch (rlk_logp_fwd_bwd)" if one_pass
+                   else "rlk_logp_fwd then rlk_logp_bwd"},
         "tokens_per_s": round(n / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": total_bytes,

@@ -158,6 +158,33 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
                         void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward and backward in one launch, for a caller that has the upstream
+ * gradient g before the forward (for instance a policy-gradient loss whose
+ * per-token weights are fixed in advance).  The outputs are bitwise those of
+ * rlk_logp_fwd followed by rlk_logp_bwd on the same arguments -- the same tile
+ * partials, the same ascending merge, the same gradient arithmetic -- for every
+ * num_virtual_shards; one block owns a row, so the row's second read (for dX)
+ * follows its first and is served by the caches: HBM sees one read of the
+ * logits and one write of dX instead of two reads and one write.  This
+ * single-pass schedule is not on the pages; the contract is [PR289]'s.
+ *   desc        as for rlk_logp_fwd, with num_vocab_tiles <= 1024 (the row's
+ *               partials live in on-chip memory); num_virtual_shards is
+ *               validated and, as everywhere, changes nothing.
+ *   logits, targets, active_mask       as for rlk_logp_fwd.
+ *   grad_logp   (device) float [N]: g, read on effective-active rows only.
+ *   logp, lse   (device) float [N] out, as for rlk_logp_fwd.
+ *   dlogits, ld_dlogits, dlogits_dtype  out, as for rlk_logp_bwd.
+ *   workspace   >= rlk_logp_fwd_bwd_workspace_bytes(desc) bytes (the 256
+ *               bytes of status words), 256-byte aligned.
+ * Errors as for rlk_logp_fwd (RLK_ERR_BAD_TILING also for T > 1024) and
+ * rlk_logp_bwd. */
+size_t rlk_logp_fwd_bwd_workspace_bytes(const rlk_logp_desc* desc);
+rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
+                            const int32_t* targets, const uint8_t* active_mask,
+                            const float* grad_logp, float* logp, float* lse, void* dlogits,
+                            int64_t ld_dlogits, rlk_dtype dlogits_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Fused LM-head variant: the logits are z = hidden . weight^T, taken in fp32
  * from bf16 MFMA products and never written to memory.  The pages name an
  * optional fused kernel without describing it ([I323] "Validation Boundary");

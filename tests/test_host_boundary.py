@@ -244,3 +244,40 @@ def test_fused_lmhead_host_validation():
     rlk.rlk_logp_fused_lmhead(desc(num_tokens=0, real_vocab=1000, padded_vocab=1024,
                                    num_vocab_tiles=4), None, None, 64, None, None, None, None,
                               None, stream=s)
+
+
+def test_fwd_bwd_host_validation():
+    a = _FakeTensor(0x10000000)
+    s = _NoStream()
+    ok = desc(num_tokens=8, num_vocab_tiles=64)
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(ok) == 256
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(desc(num_vocab_tiles=1024)) == 256
+    # the row's partials live on chip: at most 1024 tiles
+    big = desc(num_tokens=8, real_vocab=4000, padded_vocab=4096, ld_logits=4096,
+               num_vocab_tiles=1025)
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(big) == 0
+    ws = _FakeTensor(0x20000000, 256)
+    f32 = rlk.RLK_DTYPE_F32
+
+    def call(d=ok, logits=a, tgt=a, grad=a, logp=a, lse=a, dl=a, ld_d=1024, dt=f32, w=ws):
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_fwd_bwd(d, logits, tgt, None, grad, logp, lse, dl, ld_d, dt, w, stream=s)
+        return ei.value.status
+
+    assert call(d=big) == rlk.RLK_ERR_BAD_TILING
+    for kw, code in BAD_DESCS:
+        assert call(d=desc(**kw)) == code, kw
+    assert call(dt=7) == rlk.RLK_ERR_DTYPE
+    assert call(ld_d=1016) == rlk.RLK_ERR_BAD_SHAPE
+    assert call(ld_d=1028) == rlk.RLK_ERR_ALIGNMENT
+    for name in ("logits", "tgt", "grad", "logp", "lse", "dl"):
+        assert call(**{name: None}) == rlk.RLK_ERR_NULL_POINTER, name
+    assert call(w=None) == rlk.RLK_ERR_WORKSPACE
+    assert call(w=_FakeTensor(0x20000000, 255)) == rlk.RLK_ERR_WORKSPACE
+    assert call(w=_FakeTensor(0x20000040, 256)) == rlk.RLK_ERR_ALIGNMENT
+    assert call(logits=_FakeTensor(0x10000008)) == rlk.RLK_ERR_ALIGNMENT
+    assert call(dl=_FakeTensor(0x30000004)) == rlk.RLK_ERR_ALIGNMENT
+    assert call(grad=_FakeTensor(0x10000002)) == rlk.RLK_ERR_ALIGNMENT
+    # an empty batch is a no-op
+    rlk.rlk_logp_fwd_bwd(desc(num_tokens=0), None, None, None, None, None, None, None, 1024, f32,
+                         None, stream=s)

@@ -1,6 +1,6 @@
 """Build step for librlk_logp.so (hipcc, gfx950 only).
 
-Run ``python -m vocab_selected_token_amd.build_lib`` (or ``__graft_entry__.build()``).
+Run ``python vocab_selected_token_amd/build_lib.py`` (or ``__graft_entry__.build()``).
 The library is built in-tree so that it travels with the source tree.
 """
 from __future__ import annotations

@@ -267,6 +267,90 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
 }
 
 // ---------------------------------------------------------------------------
+// Forward and backward in one launch.
+// ---------------------------------------------------------------------------
+namespace {
+
+rlk_status check_fwd_bwd_desc(const rlk_logp_desc* d) {
+  rlk_status st = check_desc(d);
+  if (st != RLK_OK) return st;
+  if (d->num_vocab_tiles > rlk::kFbMaxTiles)
+    return fail(RLK_ERR_BAD_TILING, "fused forward+backward takes num_vocab_tiles <= %d (got %d)",
+                rlk::kFbMaxTiles, d->num_vocab_tiles);
+  return RLK_OK;
+}
+
+}  // namespace
+
+size_t rlk_logp_fwd_bwd_workspace_bytes(const rlk_logp_desc* desc) {
+  if (check_fwd_bwd_desc(desc) != RLK_OK) return 0;
+  return kStatusBytes;
+}
+
+rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
+                            const int32_t* targets, const uint8_t* active_mask,
+                            const float* grad_logp, float* logp, float* lse, void* dlogits,
+                            int64_t ld_dlogits, rlk_dtype dlogits_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_fwd_bwd_desc(desc);
+  if (st != RLK_OK) return st;
+  if (dlogits_dtype != RLK_DTYPE_F32 && dlogits_dtype != RLK_DTYPE_BF16)
+    return fail(RLK_ERR_DTYPE, "dlogits_dtype=%d is neither RLK_DTYPE_F32 nor RLK_DTYPE_BF16",
+                (int)dlogits_dtype);
+  if (ld_dlogits < desc->padded_vocab)
+    return fail(RLK_ERR_BAD_SHAPE, "ld_dlogits=%lld < padded_vocab=%lld", (long long)ld_dlogits,
+                (long long)desc->padded_vocab);
+  if (ld_dlogits % 8 != 0)
+    return fail(RLK_ERR_ALIGNMENT, "ld_dlogits=%lld is not a multiple of 8 elements",
+                (long long)ld_dlogits);
+  const int64_t n = desc->num_tokens;
+  if (n == 0) return ok();
+  if (!logits || !targets || !grad_logp || !logp || !lse || !dlogits)
+    return fail(RLK_ERR_NULL_POINTER, "logits, targets, grad_logp, logp, lse and dlogits must "
+                                      "be non-NULL");
+  if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < kStatusBytes)
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < %zu", workspace_bytes, kStatusBytes);
+  if (!aligned(logits, 16) || !aligned(dlogits, 16))
+    return fail(RLK_ERR_ALIGNMENT, "logits and dlogits must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  if (!aligned(targets, 4) || !aligned(grad_logp, 4) || !aligned(logp, 4) || !aligned(lse, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, grad_logp, logp and lse must be 4-byte aligned");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint32_t* status = reinterpret_cast<uint32_t*>(workspace);
+  const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
+  hipError_t e;
+  if (validate) {
+    e = rlk::launch_clear_status(status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+  }
+  const int32_t T = desc->num_vocab_tiles;
+  rlk::FwdBwdArgs a;
+  a.logits = logits;
+  a.ld = desc->ld_logits;
+  a.num_rows = (int32_t)n;
+  a.real_vocab = (int32_t)desc->real_vocab;
+  a.padded_vocab = (int32_t)desc->padded_vocab;
+  a.num_tiles = T;
+  a.tile_width = (desc->padded_vocab % T == 0) ? (int32_t)(desc->padded_vocab / T) : 0;
+  a.targets = targets;
+  a.mask = active_mask;
+  a.ignore_index = desc->ignore_index;
+  a.grad = grad_logp;
+  a.logp = logp;
+  a.lse = lse;
+  a.dlogits = dlogits;
+  a.ld_d = ld_dlogits;
+  a.out_bf16 = dlogits_dtype == RLK_DTYPE_BF16;
+  a.status = status;
+  e = rlk::launch_fwd_bwd(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "fwd_bwd_rows launch");
+  if (validate) return finish_validate(status, stream, true);
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Fused LM-head variant.
 // ---------------------------------------------------------------------------
 namespace {

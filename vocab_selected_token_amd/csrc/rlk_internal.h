@@ -56,6 +56,30 @@ struct BwdArgs {
   uint32_t* status;
 };
 
+// Forward and backward in one launch (g known before the forward): one block
+// per row keeps the row's tile partials in LDS, so T is bounded.
+constexpr int32_t kFbMaxTiles = 1024;
+
+struct FwdBwdArgs {
+  const void* logits;
+  int64_t ld;
+  int32_t num_rows;
+  int32_t real_vocab;
+  int32_t padded_vocab;
+  int32_t num_tiles;
+  int32_t tile_width;  // V_pad / T if exact, else 0
+  const int32_t* targets;
+  const uint8_t* mask;  // may be null
+  int32_t ignore_index;
+  const float* grad;
+  float* logp;
+  float* lse;
+  void* dlogits;
+  int64_t ld_d;
+  bool out_bf16;
+  uint32_t* status;
+};
+
 // Fused LM-head variant: vocabulary rows per GEMM block (tiles must be at
 // least this wide, so a block holds at most one tile bound).
 constexpr int32_t kLmheadBlockVocab = 256;
@@ -86,6 +110,7 @@ int64_t bwd_col_blocks(int32_t padded_vocab);
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_bwd(const FwdBwdArgs& a, hipStream_t stream);
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
 
 }  // namespace rlk

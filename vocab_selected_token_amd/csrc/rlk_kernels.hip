@@ -60,6 +60,17 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// A load whose line should stay in the caches (the fused forward+backward
+// reads every chunk a second time shortly afterwards).
+__device__ __forceinline__ uint4 load_keep(const uint4* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <bool kNt>
+__device__ __forceinline__ uint4 load_chunk(const uint4* p) {
+  if constexpr (kNt) return load_stream(p);
+  else return load_keep(p);
+}
 __device__ __forceinline__ void store_stream(uint4* p, const uint4& w) {
   __builtin_nontemporal_store(u32x4{w.x, w.y, w.z, w.w}, reinterpret_cast<u32x4*>(p));
 }
@@ -111,27 +122,130 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
   v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
 }
 
-// A pass with K chunk slots per lane in which some slots fall outside the
-// tile's full chunks [lo_c, hi_c): slot k of lane gl is chunk base + 16k + gl,
-// and slots outside the range hold -inf (they add exactly 0).  The load
-// address is clamped into the range, so nothing outside the tile is read.
-template <int K>
-__device__ __forceinline__ void masked_pass(const uint4* __restrict__ rowp, int32_t base,
-                                            int32_t lo_c, int32_t hi_c, int gl, float& m,
-                                            float& s) {
-  if (base >= hi_c || lo_c >= hi_c) return;  // nothing of this lane's tile here
-  uint4 q[K];
+// A pass: slot k (k < kChunks) of lane gl of the group is chunk b + 16k + gl.
+// Slots outside the tile's full chunks [lo_c, hi_c) are loaded from a clamped
+// address (nothing outside the tile is read) and hold -inf, which adds
+// exactly 0: fold_values gives the same bits as if the slot were absent.
+template <bool kNt>
+__device__ __forceinline__ void load_pass(uint4 (&q)[kChunks], const uint4* __restrict__ rowp,
+                                          int32_t b, int32_t lo_c, int32_t hi_c, int gl) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int32_t c = base + k * kGroupLanes + gl;
-    q[k] = load_stream(rowp + min(max(c, lo_c), hi_c - 1));
-    if (c < lo_c || c >= hi_c)
-      q[k] = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+  for (int k = 0; k < kChunks; ++k) {
+    const int32_t c = b + k * kGroupLanes + gl;
+    q[k] = load_chunk<kNt>(rowp + min(max(c, lo_c), hi_c - 1));
   }
-  float v[K * 8];
+}
+
+__device__ __forceinline__ void fold_pass(const uint4 (&q)[kChunks], int32_t b, int32_t lo_c,
+                                          int32_t hi_c, int gl, float& m, float& s) {
+  float v[kChunks * 8];
 #pragma unroll
-  for (int k = 0; k < K; ++k) unpack8(q[k], &v[k * 8]);
+  for (int k = 0; k < kChunks; ++k) {
+    const int32_t c = b + k * kGroupLanes + gl;
+    uint4 w = q[k];
+    if (c < lo_c || c >= hi_c)
+      w = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
+    unpack8(w, &v[k * 8]);
+  }
   fold_values(v, m, s);
+}
+
+// Columns [lo, hi) of tile `tile`: floor(t * V_pad / T) bounds (tile_width =
+// V_pad / T when T divides V_pad, else 0), cut at V_real so that padded
+// columns never count; an all-padding tile is empty.
+__device__ __forceinline__ void tile_range(int32_t tile, int32_t tile_width, int32_t padded_vocab,
+                                           int32_t num_tiles, int32_t real_vocab, int32_t& lo,
+                                           int32_t& hi) {
+  if (tile_width) {
+    lo = tile * tile_width;
+    hi = lo + tile_width;
+  } else {
+    lo = (int32_t)(((int64_t)tile * padded_vocab) / num_tiles);
+    hi = (int32_t)(((int64_t)(tile + 1) * padded_vocab) / num_tiles);
+  }
+  if (hi > real_vocab) hi = real_vocab;
+  if (hi < lo) hi = lo;
+}
+
+// (max, sumexp) of the columns [lo, hi) of one row, reduced by the 16 lanes of
+// a group (gl = lane within the group); every lane of the group returns the
+// result.  The lane mapping and the order of every operation depend only on
+// (lo, hi), so a tile gives the same bits in whatever kernel, launch or block
+// computes it:
+//   1. the chunks cut by a tile bound (head on lane 0, tail on lane 1), masked
+//      by column;
+//   2. passes of kChunks slots per lane starting on the 128-byte line (8
+//      chunks, counted from the row start) that holds the first full chunk, so
+//      that each 16-lane load covers whole lines; slots outside the full
+//      chunks are masked (leading and trailing passes);
+//   3. the 16 lanes combined by an exact max and a fixed rotate tree.
+// kNt selects the nontemporal load hint and kDepth the number of passes whose
+// loads are in flight (1 or 2); neither changes the arithmetic.
+template <bool kNt, int kDepth>
+__device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int32_t lo,
+                                             int32_t hi, int gl, float& gm_out, float& ls_out) {
+  static_assert(kDepth == 1 || kDepth == 2, "prefetch depth is 1 or 2 passes");
+  float m = kNegInf, s = 0.0f;
+  const int32_t cf_lo = (lo + 7) >> 3;  // first full chunk
+  int32_t cf_hi = hi >> 3;              // end of full chunks
+  if (cf_hi < cf_lo) cf_hi = cf_lo;
+  const int32_t base0 = cf_lo & ~7;
+  const int32_t npass = cf_hi > cf_lo ? (cf_hi - base0 + kPassChunks - 1) / kPassChunks : 0;
+
+  uint4 qa[kChunks], qb[kChunks];
+  if (kDepth == 2 && npass > 0) load_pass<kNt>(qa, rowp, base0, cf_lo, cf_hi, gl);
+  {
+    int32_t c = -1, e_lo = 0, e_hi = 0;
+    if (gl == 0 && hi > lo && (lo & 7)) {
+      c = lo >> 3;
+      e_lo = lo & 7;
+      e_hi = min(hi - (c << 3), 8);
+    } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= cf_lo) {
+      c = hi >> 3;
+      e_lo = 0;
+      e_hi = hi & 7;
+    }
+    if (c >= 0) {
+      float v[8];
+      unpack8(load_chunk<kNt>(rowp + c), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < e_lo || e >= e_hi) v[e] = kNegInf;
+      fold_values(v, m, s);
+    }
+  }
+  if (kDepth == 1) {
+    for (int32_t p = 0; p < npass; ++p) {
+      const int32_t b = base0 + p * kPassChunks;
+      load_pass<kNt>(qa, rowp, b, cf_lo, cf_hi, gl);
+      fold_pass(qa, b, cf_lo, cf_hi, gl, m, s);
+    }
+  } else {
+    // two passes in flight: the next pass's loads are issued before this one folds
+    for (int32_t p = 0; p < npass; p += 2) {
+      const int32_t b = base0 + p * kPassChunks;
+      if (p + 1 < npass) load_pass<kNt>(qb, rowp, b + kPassChunks, cf_lo, cf_hi, gl);
+      fold_pass(qa, b, cf_lo, cf_hi, gl, m, s);
+      if (p + 1 >= npass) break;
+      if (p + 2 < npass) load_pass<kNt>(qa, rowp, b + 2 * kPassChunks, cf_lo, cf_hi, gl);
+      fold_pass(qb, b + kPassChunks, cf_lo, cf_hi, gl, m, s);
+    }
+  }
+
+  float gm = m;
+  gm = maxnan(gm, row_ror<8>(gm));
+  gm = maxnan(gm, row_ror<4>(gm));
+  gm = maxnan(gm, row_ror<2>(gm));
+  gm = maxnan(gm, row_ror<1>(gm));
+  float ls = 0.0f;
+  if (gm != kNegInf && m != kNegInf) ls = s * exp2_hw((m - gm) * kLog2e);
+  ls += row_ror<8>(ls);
+  ls += row_ror<4>(ls);
+  ls += row_ror<2>(ls);
+  ls += row_ror<1>(ls);
+  if (gm == kNegInf) ls = 0.0f;  // the (-inf, 0) identity partial
+  gm_out = gm;
+  ls_out = ls;
 }
 
 // ---------------------------------------------------------------------------
@@ -168,92 +282,11 @@ __global__ __launch_bounds__(256) void stage1_partials(
   const int32_t tile = tile_begin + tq;
 
   int32_t lo = 0, hi = 0;
-  if (have) {
-    if (tile_width) {
-      lo = tile * tile_width;
-      hi = lo + tile_width;
-    } else {
-      lo = (int32_t)(((int64_t)tile * padded_vocab) / num_tiles);
-      hi = (int32_t)(((int64_t)(tile + 1) * padded_vocab) / num_tiles);
-    }
-    if (hi > real_vocab) hi = real_vocab;  // padded columns never count
-    if (hi < lo) hi = lo;                  // an all-padding tile is empty
-  }
+  if (have) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
   const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
 
-  float m = kNegInf, s = 0.0f;
-
-  // chunks cut by a tile bound: the head (lo not 16-byte aligned) goes to
-  // lane 0 of the group, the tail (hi not aligned) to lane 1
-  const int32_t cf_lo = (lo + 7) >> 3;  // first full chunk
-  int32_t cf_hi = hi >> 3;              // end of full chunks
-  if (cf_hi < cf_lo) cf_hi = cf_lo;
-  {
-    int32_t c = -1, e_lo = 0, e_hi = 0;
-    if (gl == 0 && hi > lo && (lo & 7)) {
-      c = lo >> 3;
-      e_lo = lo & 7;
-      e_hi = min(hi - (c << 3), 8);
-    } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= cf_lo) {
-      c = hi >> 3;
-      e_lo = 0;
-      e_hi = hi & 7;
-    }
-    if (c >= 0) {
-      float v[8];
-      unpack8(load_stream(rowp + c), v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < e_lo || e >= e_hi) v[e] = kNegInf;
-      fold_values(v, m, s);
-    }
-  }
-
-  // Full chunks [cf_lo, cf_hi).  Passes start on the 128-byte line (8 chunks,
-  // counted from the row start) that holds cf_lo, so that each 16-lane load
-  // covers whole lines and no line is split between two loads of a group; a
-  // leading pass masks the chunks in front of cf_lo.  Then whole passes, then
-  // a remainder pass of as many slots as the wave's widest remainder needs
-  // (1..kChunks).  The mapping depends only on the tile's columns.
-  int32_t base = cf_lo & ~7;
-  if (base < cf_lo) {
-    masked_pass<kChunks>(rowp, base, cf_lo, cf_hi, gl, m, s);
-    base += kPassChunks;
-  }
-  for (; base + kPassChunks <= cf_hi; base += kPassChunks) {
-    uint4 q[kChunks];
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) q[k] = load_stream(rowp + base + k * kGroupLanes + gl);
-    float v[kChunks * 8];
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) unpack8(q[k], &v[k * 8]);
-    fold_values(v, m, s);
-  }
-  int32_t slots = base < cf_hi ? (cf_hi - base + kGroupLanes - 1) / kGroupLanes : 0;
-  slots = max(max(__builtin_amdgcn_readlane(slots, 0), __builtin_amdgcn_readlane(slots, 16)),
-              max(__builtin_amdgcn_readlane(slots, 32), __builtin_amdgcn_readlane(slots, 48)));
-  switch (slots) {
-    case 1: masked_pass<1>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
-    case 2: masked_pass<2>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
-    case 3: masked_pass<3>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
-    case 4: masked_pass<4>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
-    case 5: masked_pass<5>(rowp, base, cf_lo, cf_hi, gl, m, s); break;
-    default: break;
-  }
-
-  // combine the 16 lanes of the group: exact max, then a fixed rotate tree
-  float gm = m;
-  gm = maxnan(gm, row_ror<8>(gm));
-  gm = maxnan(gm, row_ror<4>(gm));
-  gm = maxnan(gm, row_ror<2>(gm));
-  gm = maxnan(gm, row_ror<1>(gm));
-  float ls = 0.0f;
-  if (gm != kNegInf && m != kNegInf) ls = s * exp2_hw((m - gm) * kLog2e);
-  ls += row_ror<8>(ls);
-  ls += row_ror<4>(ls);
-  ls += row_ror<2>(ls);
-  ls += row_ror<1>(ls);
-  if (gm == kNegInf) ls = 0.0f;  // the (-inf, 0) identity partial
+  float gm, ls;
+  tile_partial<true, 2>(rowp, lo, hi, gl, gm, ls);
 
   if (have && gl == 0) {
     const int64_t o = (int64_t)row * num_tiles + tile;
@@ -384,6 +417,44 @@ struct Store8<uint16_t> {
   }
 };
 
+// dX of the 8 columns [j0, j0 + 8) of one row (q = their logits, read only on
+// an effective-active row with a good target and j0 < V_real):
+//   inactive row                 +0
+//   bad target                   NaN on real columns, +0 on padded ones
+//   real column j                -g * exp(x_j - L), and g * (1 - exp(x_t - L))
+//                                at the target t
+//   padded column                +0
+// exp(y) is taken as exp2(y * log2 e) on the hardware unit, in one fixed form.
+__device__ __forceinline__ void dlogits_chunk(const uint4& q, int32_t j0, bool act, bool bad,
+                                              float L, float g, int32_t tgt, int32_t real_vocab,
+                                              float (&d)[8]) {
+  if (!act) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+  } else if (bad) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
+  } else if (j0 >= real_vocab) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+  } else {
+    float x[8];
+    unpack8(q, x);
+    const float ng = -g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
+    if (j0 + 8 > real_vocab) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e >= real_vocab) d[e] = 0.0f;
+    }
+    if (tgt >= j0 && tgt < j0 + 8) {
+      const int e = tgt - j0;
+      d[e] = g * (1.0f - exp2_hw((x[e] - L) * kLog2e));
+    }
+  }
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
@@ -418,32 +489,168 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
     const int32_t j0 = c << 3;
     if (j0 >= padded_vocab) continue;
     float d[8];
-    if (!act) {
+    dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
+    Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward and backward in one launch, for a caller that knows g before the
+// forward.  One block owns one row:
+//   1. its 4 * kFbWaves groups compute the row's T tile partials with the
+//      stage-1 code (tile t on group t mod groups), into LDS; the target logit
+//      is gathered first and the first batch of phase-3 loads is issued before
+//      the barrier, so both are in flight during the merge;
+//   2. wave 0 merges the partials in ascending tile order (the stage-2
+//      arithmetic) and writes LSE, logp and the status words;
+//   3. the whole block streams the row again, one batch of loads ahead, and
+//      writes dX.
+// The second read follows the first within tens of microseconds, so it is
+// served by the caches (the first read does not carry the nontemporal hint)
+// and HBM sees one read and one write of the row.  Every value is computed by
+// the same code, in the same order, as in stage1_partials, stage2_merge and
+// bwd_dlogits, so the outputs are bitwise those of the separate launches.
+// ---------------------------------------------------------------------------
+constexpr int kFbWaves = 8;
+constexpr int kFbThreads = kFbWaves * 64;
+constexpr int kFbGroups = kFbWaves * kGroupsPerWave;
+constexpr int kFbUnroll = 4;
+
+// The stage-2 merge of T <= 64 partials held one per lane of a wave (lane t
+// holds tile t; lanes >= T hold the identity).  The max is exact in any order
+// and the exponentials are taken in parallel; the fmaf chain then runs in
+// ascending tile order over LDS copies, as in merge_row.  An identity partial
+// enters the chain as fmaf(0, 0, S), which is S (S >= +0), exactly as if it
+// were skipped.  Every lane returns the LSE.
+__device__ __forceinline__ float merge_lanes(float mt, float st, int32_t num_tiles, int lane,
+                                             float* s_e, float* s_sv) {
+  float M = mt;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = 0.0f;
-    } else if (bad) {
+  for (int o = 32; o >= 1; o >>= 1) M = maxnan(M, __shfl_xor(M, o));
+  if (M == kNegInf) return kNegInf;
+  const bool live = lane < num_tiles && mt != kNegInf;
+  s_e[lane] = live ? expf(mt - M) : 0.0f;
+  s_sv[lane] = live ? st : 0.0f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float S = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
-    } else if (j0 >= real_vocab) {
+  for (int t = 0; t < 64; t += 4) {
+    const float4 e4 = *reinterpret_cast<const float4*>(s_e + t);
+    const float4 s4 = *reinterpret_cast<const float4*>(s_sv + t);
+    S = fmaf(s4.x, e4.x, S);
+    S = fmaf(s4.y, e4.y, S);
+    S = fmaf(s4.z, e4.z, S);
+    S = fmaf(s4.w, e4.w, S);
+  }
+  return M + logf(S);
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
+    const uint4* __restrict__ logits, int64_t ld_chunks, int32_t real_vocab,
+    int32_t padded_vocab, int32_t num_tiles, int32_t tile_width,
+    const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
+    const float* __restrict__ grad, float* __restrict__ logp, float* __restrict__ lse,
+    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status) {
+  __shared__ float s_m[kFbMaxTiles];
+  __shared__ float s_s[kFbMaxTiles];
+  __shared__ __align__(16) float s_e[64];
+  __shared__ __align__(16) float s_sv[64];
+  __shared__ float s_lse;
+  const int32_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave * kGroupsPerWave + (lane >> 4);
+  const int gl = lane & 15;
+  const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
+
+  const bool act_mask = (mask == nullptr || mask[row] != 0);
+  const int32_t tgt = act_mask ? targets[row] : 0;
+  const bool act = act_mask && tgt != ignore_index;
+  const bool bad = act && (tgt < 0 || tgt >= real_vocab);
+  const bool reread = act && !bad;
+  float x_t = 0.0f;
+  if (wave == 0 && reread)
+    x_t = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rowp)[tgt] << 16);
+  const float g = act ? grad[row] : 0.0f;
+
+  // 1. tile partials (the loop bound is uniform: all groups of a wave call
+  //    tile_partial together)
+  for (int32_t t0 = 0; t0 < num_tiles; t0 += kFbGroups) {
+    const int32_t tile = t0 + grp;
+    int32_t lo = 0, hi = 0;
+    if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
+    float gm, ls;
+    tile_partial<false, 1>(rowp, lo, hi, gl, gm, ls);
+    if (tile < num_tiles && gl == 0) {
+      s_m[tile] = gm;
+      s_s[tile] = ls;
+    }
+  }
+  const int32_t n_chunks = (padded_vocab + 7) >> 3;
+  int32_t c0 = threadIdx.x;
+  uint4 qa[kFbUnroll], qb[kFbUnroll];
+  if (reread) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int k = 0; k < kFbUnroll; ++k) {
+      const int32_t c = c0 + k * kFbThreads;
+      if ((c << 3) < real_vocab) qa[k] = load_stream(rowp + c);
+    }
+  }
+  __syncthreads();
+
+  // 2. merge, LSE, logp (wave 0)
+  if (wave == 0) {
+    float L;
+    if (num_tiles <= 64) {
+      const float mt = lane < num_tiles ? s_m[lane] : kNegInf;
+      const float st = lane < num_tiles ? s_s[lane] : 0.0f;
+      L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
     } else {
-      float x[8];
-      unpack8(q[k], x);
-      const float ng = -g;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
-      if (j0 + 8 > real_vocab) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (j0 + e >= real_vocab) d[e] = 0.0f;
-      }
-      if (tgt >= j0 && tgt < j0 + 8) {
-        const int e = tgt - j0;
-        d[e] = g * (1.0f - exp2_hw((x[e] - L) * kLog2e));
+      L = merge_row(s_m, s_s, num_tiles);
+    }
+    if (lane == 0) {
+      s_lse = L;
+      lse[row] = L;
+      if (!act) {
+        logp[row] = 0.0f;
+      } else if (bad) {
+        logp[row] = __builtin_nanf("");
+        status[0] = 1u;
+      } else {
+        logp[row] = x_t - L;
+        if (!__builtin_isfinite(L)) status[1] = 1u;
       }
     }
-    Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
+  }
+  __syncthreads();
+
+  // 3. dX over the row's V_pad columns (the logits of inactive or bad rows
+  //    are not read again)
+  const float L = act ? s_lse : 0.0f;
+  OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
+  for (; c0 < n_chunks; c0 += kFbThreads * kFbUnroll) {
+    const int32_t c1 = c0 + kFbThreads * kFbUnroll;
+    if (reread && c1 < n_chunks) {
+#pragma unroll
+      for (int k = 0; k < kFbUnroll; ++k) {
+        const int32_t c = c1 + k * kFbThreads;
+        if ((c << 3) < real_vocab) qb[k] = load_stream(rowp + c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kFbUnroll; ++k) {
+      const int32_t c = c0 + k * kFbThreads;
+      const int32_t j0 = c << 3;
+      if (j0 >= padded_vocab) continue;
+      float d[8];
+      dlogits_chunk(qa[k], j0, act, bad, L, g, tgt, real_vocab, d);
+      Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
+    }
+#pragma unroll
+    for (int k = 0; k < kFbUnroll; ++k) qa[k] = qb[k];
   }
 }
 
@@ -502,6 +709,24 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
                        a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets, a.mask,
                        a.ignore_index, a.lse, a.grad, reinterpret_cast<float*>(a.dlogits),
                        a.ld_d, a.status);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bwd(const FwdBwdArgs& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.num_rows);
+  const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  if (a.out_bf16) {
+    hipLaunchKernelGGL(fwd_bwd_rows<uint16_t>, grid, dim3(kFbThreads), 0, stream, x, a.ld / 8,
+                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.targets,
+                       a.mask, a.ignore_index, a.grad, a.logp, a.lse,
+                       reinterpret_cast<uint16_t*>(a.dlogits), a.ld_d, a.status);
+  } else {
+    hipLaunchKernelGGL(fwd_bwd_rows<float>, grid, dim3(kFbThreads), 0, stream, x, a.ld / 8,
+                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.targets,
+                       a.mask, a.ignore_index, a.grad, a.logp, a.lse,
+                       reinterpret_cast<float*>(a.dlogits), a.ld_d, a.status);
   }
   return hipGetLastError();
 }
