@@ -101,14 +101,23 @@ class Oracle:
         bwd_args = [vp, i64, i64, i64, i64, vp, vp, i32, vp, vp, vp, i64, vp, ctypes.c_int]
         lib.rlk_oracle_bwd_f64.argtypes = bwd_args
         lib.rlk_oracle_bwd_bf16.argtypes = bwd_args
-        part_args = [vp, i64, i64, i64, i64, i32, vp, vp, ctypes.c_int]
+        part_args = [vp, i64, i64, i64, i64, i32, vp, vp, vp, ctypes.c_int]
         lib.rlk_oracle_tile_partials_f64.argtypes = part_args
         lib.rlk_oracle_tile_partials_bf16.argtypes = part_args
+        ent_args = [vp, i64, i64, i64, vp, ctypes.c_int]
+        lib.rlk_oracle_entropy_f64.argtypes = ent_args
+        lib.rlk_oracle_entropy_bf16.argtypes = ent_args
+        bwd_ex_args = [vp, i64, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp,
+                       ctypes.c_int]
+        lib.rlk_oracle_bwd_ex_f64.argtypes = bwd_ex_args
+        lib.rlk_oracle_bwd_ex_bf16.argtypes = bwd_ex_args
         lib.rlk_oracle_lmhead_logits.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, ctypes.c_int]
         lib.rlk_oracle_lmhead_logits.restype = ctypes.c_int
         for name in ("rlk_oracle_tile_bounds", "rlk_oracle_shard_tiles", "rlk_oracle_fwd_f64",
                      "rlk_oracle_fwd_bf16", "rlk_oracle_bwd_f64", "rlk_oracle_bwd_bf16",
-                     "rlk_oracle_tile_partials_f64", "rlk_oracle_tile_partials_bf16"):
+                     "rlk_oracle_tile_partials_f64", "rlk_oracle_tile_partials_bf16",
+                     "rlk_oracle_entropy_f64", "rlk_oracle_entropy_bf16", "rlk_oracle_bwd_ex_f64",
+                     "rlk_oracle_bwd_ex_bf16"):
             getattr(lib, name).restype = ctypes.c_int
         self._lib = lib
         self.path = Path(lib_path)
@@ -168,6 +177,40 @@ class Oracle:
             raise OracleError(rc, bad.value)
         return d
 
+    def entropy(self, x, *, real_vocab: int, nthreads: int = 0) -> np.ndarray:
+        """H_r = -sum p log p over the real columns (fp64); NaN where LSE is not finite."""
+        x, is_bf16 = _logits(x)
+        n, ld = x.shape
+        ent = np.empty(n, dtype=np.float64)
+        fn = self._lib.rlk_oracle_entropy_bf16 if is_bf16 else self._lib.rlk_oracle_entropy_f64
+        rc = fn(_ptr(x), n, real_vocab, ld, _ptr(ent), nthreads)
+        if rc:
+            raise OracleError(rc, -1)
+        return ent
+
+    def bwd_ex(self, x, tgt, mask, lse, *, real_vocab: int, padded_vocab: int, ent=None, g=None,
+               g_lse=None, g_ent=None, ignore_index: int = -100, nthreads: int = 0,
+               raise_on_error: bool = True):
+        """d = a g (onehot - p) + g_lse p - g_ent p (log p + H), fp64 [N, padded_vocab].
+        g, g_lse, g_ent may be None (zero); ent is needed when g_ent is given."""
+        x, is_bf16 = _logits(x)
+        n, ld = x.shape
+        tgt, mask = _prep_rows(tgt, mask, n)
+
+        def vec(v):
+            return None if v is None else np.ascontiguousarray(
+                np.asarray(v, dtype=np.float64).reshape(-1))
+        lse, ent, g, g_lse, g_ent = vec(lse), vec(ent), vec(g), vec(g_lse), vec(g_ent)
+        d = np.empty((n, padded_vocab), dtype=np.float64)
+        bad = ctypes.c_int64(-1)
+        fn = self._lib.rlk_oracle_bwd_ex_bf16 if is_bf16 else self._lib.rlk_oracle_bwd_ex_f64
+        rc = fn(_ptr(x), n, real_vocab, padded_vocab, ld, _ptr(tgt), _ptr(mask), ignore_index,
+                _ptr(lse), _ptr(ent), _ptr(g), _ptr(g_lse), _ptr(g_ent), _ptr(d), padded_vocab,
+                ctypes.byref(bad), nthreads)
+        if rc == ERR_ARG or (rc and raise_on_error):
+            raise OracleError(rc, bad.value)
+        return d
+
     def lmhead_logits(self, h, w, *, real_vocab: int, nthreads: int = 0) -> np.ndarray:
         """z = h . W^T in fp64 over W's first real_vocab rows.  h: [N, K], W: [V, K],
         both bf16 bit patterns (uint16).  Returns [N, real_vocab] float64."""
@@ -193,19 +236,21 @@ class Oracle:
                         nthreads=nthreads, raise_on_error=raise_on_error)
 
     def tile_partials(self, x, *, real_vocab: int, padded_vocab: int, num_tiles: int,
-                      nthreads: int = 0):
-        """Per-tile (max, sumexp) over each tile's real columns, fp64, each [N, T]."""
+                      nthreads: int = 0, with_entropy: bool = False):
+        """Per-tile (max, sumexp) over each tile's real columns, fp64, each [N, T]; with
+        with_entropy also the per-tile sum of exp(x - m) (x - m)."""
         x, is_bf16 = _logits(x)
         n, ld = x.shape
         pmax = np.empty((n, num_tiles), dtype=np.float64)
         psum = np.empty((n, num_tiles), dtype=np.float64)
+        pent = np.empty((n, num_tiles), dtype=np.float64) if with_entropy else None
         fn = (self._lib.rlk_oracle_tile_partials_bf16 if is_bf16
               else self._lib.rlk_oracle_tile_partials_f64)
         rc = fn(_ptr(x), n, real_vocab, padded_vocab, ld, num_tiles, _ptr(pmax), _ptr(psum),
-                nthreads)
+                _ptr(pent), nthreads)
         if rc:
             raise OracleError(rc, -1)
-        return pmax, psum
+        return (pmax, psum, pent) if with_entropy else (pmax, psum)
 
 
 _default: Oracle | None = None

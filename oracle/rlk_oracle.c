@@ -46,6 +46,22 @@
  *   - A non-finite LSE on an effective-active row is an error ([PR289] apply():
  *     logits over the real vocabulary must be finite for every active token).
  *
+ * Side outputs and extra gradients (entropy_row, bwd_ex_row below):
+ *
+ *   H_r    = -sum_{j < V_real} p_rj log p_rj,   p_rj = exp(x_rj - LSE_r),
+ *            with 0 log 0 = 0 (a column at -inf contributes nothing)
+ *   d_rj   = a_r g_r ([j == tgt_r] - p_rj) + gl_r p_rj - gh_r p_rj (log p_rj + H_r)
+ *
+ * The pages return the LSE as a direct diagnostic next to the selected logp
+ * ([PR289] walkthrough: forward_with_lse), and the RL runs log the mean
+ * entropy ([H100V] "H100 canonical TP/CP validation": log metrics such as mean
+ * loss/entropy).  Readings: the LSE and entropy terms apply to every row (both
+ * are defined on every row, as the LSE output is); the logp term only to
+ * effective-active rows; a row whose real logits are all -inf has no
+ * distribution, so its H is NaN, and so is any LSE or entropy gradient that
+ * reaches it.  The entropy gradient is the derivative of the definition:
+ * dH/dx_j = -p_j (log p_j + H).
+ *
  * Parity pins: every function below is pinned by tests that do not use this
  * file's arithmetic (pure-Python brute force, closed forms, finite differences,
  * float64 library routines); see tests/test_oracle_pins.py.
@@ -149,6 +165,9 @@ struct job {
   int32_t ignore_index;
   const double* lse_in;
   const double* g;
+  const double* ent_in; /* H per row (extended backward) */
+  const double* gl;     /* d loss / d LSE per row, or NULL */
+  const double* gh;     /* d loss / d H per row, or NULL */
   int32_t num_tiles;
   const int64_t* bounds;
   /* outputs */
@@ -157,6 +176,8 @@ struct job {
   double* d;
   double* pmax;
   double* psum;
+  double* pent; /* per-tile sum of exp(x - m) (x - m), or NULL */
+  double* ent;  /* H per row out */
   row_fn fn;
   /* per-thread */
   int64_t r0, r1;
@@ -217,24 +238,80 @@ static void bwd_row(const job* cjb, int64_t r, double* scratch) {
   }
 }
 
+/* Entropy of row r by the definition: LSE first (row_lse), then
+ * -sum p_j log p_j over the real columns in ascending order, skipping p_j = 0
+ * terms whose x_j is -inf (0 log 0 = 0). */
+static void entropy_row(const job* cjb, int64_t r, double* scratch) {
+  const job* jb = cjb;
+  const double* x = get_row(jb, r, scratch, jb->real_vocab);
+  double lse = row_lse(x, jb->real_vocab);
+  if (!isfinite(lse)) {
+    jb->ent[r] = NAN; /* no distribution (all -inf), or NaN / +inf inputs */
+    return;
+  }
+  double h = 0.0;
+  for (int64_t j = 0; j < jb->real_vocab; ++j) {
+    if (x[j] == -INFINITY) continue;
+    double lp = x[j] - lse;
+    h -= exp(lp) * lp;
+  }
+  jb->ent[r] = h;
+}
+
+/* The extended backward of row r: the logp term on effective-active rows,
+ * the LSE and entropy terms on every row where their upstream gradient is
+ * given and nonzero. */
+static void bwd_ex_row(const job* cjb, int64_t r, double* scratch) {
+  job* jb = (job*)cjb;
+  double* d = jb->d + r * jb->ldd;
+  for (int64_t j = 0; j < jb->padded_vocab; ++j) d[j] = 0.0;
+  const int act = row_active(jb->mask, jb->tgt, r, jb->ignore_index);
+  const double g = (act && jb->g) ? jb->g[r] : 0.0;
+  const double gl = jb->gl ? jb->gl[r] : 0.0;
+  const double gh = jb->gh ? jb->gh[r] : 0.0;
+  int32_t t = act ? jb->tgt[r] : -1;
+  if (act && (t < 0 || (int64_t)t >= jb->real_vocab)) {
+    for (int64_t j = 0; j < jb->real_vocab; ++j) d[j] = NAN;
+    note_error(jb, ORC_ERR_TARGET_RANGE, r);
+    return;
+  }
+  if (!act && gl == 0.0 && gh == 0.0) return;
+  const double* x = get_row(jb, r, scratch, jb->real_vocab);
+  const double lse = jb->lse_in[r];
+  const double h = gh != 0.0 ? jb->ent_in[r] : 0.0;
+  for (int64_t j = 0; j < jb->real_vocab; ++j) {
+    const double oh = (j == (int64_t)t) ? 1.0 : 0.0;
+    const double p = exp(x[j] - lse);
+    double v = g * (oh - p) + gl * p;
+    if (gh != 0.0 && !(x[j] == -INFINITY && isfinite(lse))) v -= gh * p * ((x[j] - lse) + h);
+    d[j] = v;
+  }
+}
+
 static void partials_row(const job* cjb, int64_t r, double* scratch) {
   const job* jb = cjb;
   const double* x = get_row(jb, r, scratch, jb->real_vocab);
   for (int32_t t = 0; t < jb->num_tiles; ++t) {
     int64_t lo = jb->bounds[t], hi = jb->bounds[t + 1];
     if (hi > jb->real_vocab) hi = jb->real_vocab; /* padded columns never count */
-    double m = -INFINITY, s = 0.0;
+    double m = -INFINITY, s = 0.0, a = 0.0;
     if (hi > lo) {
       m = span_max(x + lo, hi - lo);
       if (isnan(m)) {
         s = NAN;
+        a = NAN;
       } else if (m != -INFINITY) {
-        for (int64_t j = lo; j < hi; ++j) s += exp(x[j] - m);
+        for (int64_t j = lo; j < hi; ++j) {
+          if (x[j] == -INFINITY) continue; /* exp(-inf) = 0 and 0 (-inf) counts as 0 */
+          s += exp(x[j] - m);
+          a += exp(x[j] - m) * (x[j] - m);
+        }
       }
-      /* m == -inf: the (-inf, 0) identity partial */
+      /* m == -inf: the (-inf, 0) identity partial (and a = 0) */
     }
     jb->pmax[r * jb->num_tiles + t] = m;
     jb->psum[r * jb->num_tiles + t] = s;
+    if (jb->pent) jb->pent[r * jb->num_tiles + t] = a;
   }
 }
 
@@ -483,7 +560,7 @@ int rlk_oracle_lmhead_logits(const uint16_t* h, const uint16_t* w, int64_t n_row
  * the (-inf, 0) identity).  Used only to pin the GPU's stage-1 statistic. */
 static int partials_impl(const double* xd, const uint16_t* xb, int64_t n_rows,
                          int64_t real_vocab, int64_t padded_vocab, int64_t ld, int32_t num_tiles,
-                         double* pmax, double* psum, int nthreads) {
+                         double* pmax, double* psum, double* pent, int nthreads) {
   if (n_rows < 0 || real_vocab < 1 || padded_vocab < real_vocab || ld < padded_vocab)
     return ORC_ERR_ARG;
   if (num_tiles < 1 || (int64_t)num_tiles > padded_vocab) return ORC_ERR_ARG;
@@ -504,22 +581,109 @@ static int partials_impl(const double* xd, const uint16_t* xb, int64_t n_rows,
   jb.bounds = bounds;
   jb.pmax = pmax;
   jb.psum = psum;
+  jb.pent = pent;
   jb.fn = partials_row;
   int rc = run_rows(&jb, nthreads, NULL);
   free(bounds);
   return rc;
 }
 
+/* pent (may be NULL): per tile, sum of exp(x - m) (x - m) over the tile's
+ * real finite columns -- the entropy's per-tile statistic. */
 int rlk_oracle_tile_partials_f64(const double* x, int64_t n_rows, int64_t real_vocab,
                                  int64_t padded_vocab, int64_t ld, int32_t num_tiles,
-                                 double* pmax, double* psum, int nthreads) {
+                                 double* pmax, double* psum, double* pent, int nthreads) {
   return partials_impl(x, NULL, n_rows, real_vocab, padded_vocab, ld, num_tiles, pmax, psum,
-                       nthreads);
+                       pent, nthreads);
 }
 
 int rlk_oracle_tile_partials_bf16(const uint16_t* x, int64_t n_rows, int64_t real_vocab,
                                   int64_t padded_vocab, int64_t ld, int32_t num_tiles,
-                                  double* pmax, double* psum, int nthreads) {
+                                  double* pmax, double* psum, double* pent, int nthreads) {
   return partials_impl(NULL, x, n_rows, real_vocab, padded_vocab, ld, num_tiles, pmax, psum,
-                       nthreads);
+                       pent, nthreads);
+}
+
+/* Entropy H_r of every row (fp64), by the definition in the header. */
+static int entropy_impl(const double* xd, const uint16_t* xb, int64_t n_rows,
+                        int64_t real_vocab, int64_t ld, double* ent, int nthreads) {
+  if (n_rows < 0 || real_vocab < 1 || ld < real_vocab) return ORC_ERR_ARG;
+  if (n_rows == 0) return ORC_OK;
+  if ((!xd && !xb) || !ent) return ORC_ERR_ARG;
+  job jb;
+  memset(&jb, 0, sizeof jb);
+  jb.xd = xd;
+  jb.xb = xb;
+  jb.n_rows = n_rows;
+  jb.real_vocab = real_vocab;
+  jb.ld = ld;
+  jb.ent = ent;
+  jb.fn = entropy_row;
+  return run_rows(&jb, nthreads, NULL);
+}
+
+int rlk_oracle_entropy_f64(const double* x, int64_t n_rows, int64_t real_vocab, int64_t ld,
+                           double* ent, int nthreads) {
+  return entropy_impl(x, NULL, n_rows, real_vocab, ld, ent, nthreads);
+}
+
+int rlk_oracle_entropy_bf16(const uint16_t* x, int64_t n_rows, int64_t real_vocab, int64_t ld,
+                            double* ent, int nthreads) {
+  return entropy_impl(NULL, x, n_rows, real_vocab, ld, ent, nthreads);
+}
+
+/* The extended backward: d = a g (onehot - p) + gl p - gh p (log p + H) on the
+ * real columns, 0 on the padded ones.  g, gl, gh may each be NULL (zero); ent
+ * is read only where gh is given.  Errors as for the plain backward. */
+static int bwd_ex_impl(const double* xd, const uint16_t* xb, int64_t n_rows, int64_t real_vocab,
+                       int64_t padded_vocab, int64_t ld, const int32_t* tgt, const uint8_t* mask,
+                       int32_t ignore_index, const double* lse, const double* ent,
+                       const double* g, const double* gl, const double* gh, double* d,
+                       int64_t ldd, int64_t* bad_row, int nthreads) {
+  if (bad_row) *bad_row = -1;
+  int rc = check_common(n_rows, real_vocab, ld, xd ? (const void*)xd : (const void*)xb, tgt);
+  if (rc) return rc;
+  if (padded_vocab < real_vocab || ldd < padded_vocab) return ORC_ERR_ARG;
+  if (n_rows == 0) return ORC_OK;
+  if (!lse || !d || (gh && !ent)) return ORC_ERR_ARG;
+  job jb;
+  memset(&jb, 0, sizeof jb);
+  jb.xd = xd;
+  jb.xb = xb;
+  jb.n_rows = n_rows;
+  jb.real_vocab = real_vocab;
+  jb.padded_vocab = padded_vocab;
+  jb.ld = ld;
+  jb.ldd = ldd;
+  jb.tgt = tgt;
+  jb.mask = mask;
+  jb.ignore_index = ignore_index;
+  jb.lse_in = lse;
+  jb.ent_in = ent;
+  jb.g = g;
+  jb.gl = gl;
+  jb.gh = gh;
+  jb.d = d;
+  jb.fn = bwd_ex_row;
+  return run_rows(&jb, nthreads, bad_row);
+}
+
+int rlk_oracle_bwd_ex_f64(const double* x, int64_t n_rows, int64_t real_vocab,
+                          int64_t padded_vocab, int64_t ld, const int32_t* tgt,
+                          const uint8_t* mask, int32_t ignore_index, const double* lse,
+                          const double* ent, const double* g, const double* gl,
+                          const double* gh, double* d, int64_t ldd, int64_t* bad_row,
+                          int nthreads) {
+  return bwd_ex_impl(x, NULL, n_rows, real_vocab, padded_vocab, ld, tgt, mask, ignore_index, lse,
+                     ent, g, gl, gh, d, ldd, bad_row, nthreads);
+}
+
+int rlk_oracle_bwd_ex_bf16(const uint16_t* x, int64_t n_rows, int64_t real_vocab,
+                           int64_t padded_vocab, int64_t ld, const int32_t* tgt,
+                           const uint8_t* mask, int32_t ignore_index, const double* lse,
+                           const double* ent, const double* g, const double* gl,
+                           const double* gh, double* d, int64_t ldd, int64_t* bad_row,
+                           int nthreads) {
+  return bwd_ex_impl(NULL, x, n_rows, real_vocab, padded_vocab, ld, tgt, mask, ignore_index, lse,
+                     ent, g, gl, gh, d, ldd, bad_row, nthreads);
 }

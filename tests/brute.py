@@ -75,3 +75,54 @@ def partials(row, bounds, real_vocab):
         else:
             out.append((m, math.fsum(math.exp(x - m) for x in xs)))
     return out
+
+
+def entropy(xs) -> float:
+    """H = -sum p log p with exactly rounded sums; p = 0 terms contribute 0."""
+    z = normaliser(xs)
+    if z == 0.0:
+        return math.nan
+    terms = []
+    for x in xs:
+        if x == -math.inf:
+            continue
+        p = math.exp(x) / z
+        if p > 0.0:
+            terms.append(-p * math.log(p))
+    return math.fsum(terms)
+
+
+def bwd_ex(rows, tgt, mask, g, g_lse, g_ent, real_vocab, padded_vocab, ignore_index=-100):
+    """d = a g (onehot - p) + g_lse p - g_ent p (log p + H); g, g_lse, g_ent may be None."""
+    out = []
+    for r, row in enumerate(rows):
+        d = [0.0] * padded_vocab
+        xs = list(row[:real_vocab])
+        act = active(mask, tgt, r, ignore_index)
+        gr = g[r] if (g is not None and act) else 0.0
+        gl = g_lse[r] if g_lse is not None else 0.0
+        gh = g_ent[r] if g_ent is not None else 0.0
+        if act or gl != 0.0 or gh != 0.0:
+            p = probs(xs)
+            h = entropy(xs)
+            for j in range(real_vocab):
+                oh = 1.0 if (act and j == int(tgt[r])) else 0.0
+                v = gr * (oh - p[j]) + gl * p[j]
+                if gh != 0.0 and p[j] > 0.0:
+                    v -= gh * p[j] * (math.log(p[j]) + h)
+                d[j] = v
+        out.append(d)
+    return out
+
+
+def entropy_partials(row, bounds, real_vocab):
+    """Per-tile sum of exp(x - m) (x - m) over the tile's finite real columns."""
+    out = []
+    for t in range(len(bounds) - 1):
+        xs = [x for x in row[bounds[t]:min(bounds[t + 1], real_vocab)] if x != -math.inf]
+        if not xs:
+            out.append(0.0)
+            continue
+        m = max(xs)
+        out.append(math.fsum(math.exp(x - m) * (x - m) for x in xs))
+    return out

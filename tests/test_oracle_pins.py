@@ -323,8 +323,130 @@ def pin_lmhead(o):
     close(lp, ref[np.arange(n), tgt] - ls_ref, 1e-12)
 
 
+def pin_entropy(o):
+    """H = -sum p log p: brute force, closed forms, a float64 library routine, shift
+    invariance, and the bf16 path against the f64 path on decoded values."""
+    rng = np.random.default_rng(31)
+    for v in (1, 2, 3, 7, 64):
+        bits = random_bf16(rng, (4, v))
+        x = decode(bits)
+        want = [brute.entropy(list(row)) for row in x]
+        close(o.entropy(bits, real_vocab=v), want, 1e-12)
+        close(o.entropy(x, real_vocab=v), want, 1e-12)
+    v = 151936
+    x = np.zeros((6, v))
+    x[1] = 3.5                      # uniform: H = log V
+    x[2] = -np.inf
+    x[2, 17] = 2.0                  # one finite value: H = 0
+    x[3] = -np.inf
+    x[3, [5, 99, 70000]] = -1.25    # three equal finite values: H = log 3
+    x[4] = -np.inf                  # no distribution: NaN
+    x[5, :2] = [0.0, math.log(3.0)]  # p = (1/4, 3/4) over 2 columns
+    x[5, 2:] = -np.inf
+    h = o.entropy(x, real_vocab=v)
+    close(h[:2], [LN_151936, LN_151936], 1e-9)
+    assert h[2] == 0.0
+    close(h[3], math.log(3.0), 1e-12)
+    assert math.isnan(h[4])
+    close(h[5], -(0.25 * math.log(0.25) + 0.75 * math.log(0.75)), 1e-12)
+    # float64 library routine and shift invariance
+    y = rng.normal(0.0, 3.0, size=(24, 1000))
+    lib = torch.distributions.Categorical(logits=torch.from_numpy(y)).entropy().numpy()
+    close(o.entropy(y, real_vocab=1000), lib, 1e-10)
+    close(o.entropy(y + 40.0, real_vocab=1000), lib, 1e-10)
+    # padding and ld: only the real columns count
+    z = np.full((3, 48), np.nan)
+    z[:, :37] = rng.normal(size=(3, 37))
+    close(o.entropy(z, real_vocab=37),
+          [brute.entropy(list(row[:37])) for row in z], 1e-12)
+
+
+def pin_gradient_ex(o):
+    """The extended backward against float64 autograd of
+    F = sum_r [a_r g_r logp_r + gl_r LSE_r + gh_r H_r], against brute force on tiny
+    rows, and against central differences of the oracle's own forward and entropy."""
+    rng = np.random.default_rng(37)
+    n, v_real, v_pad = 7, 40, 48
+    x = rng.normal(0.0, 2.0, size=(n, v_pad))
+    x[:, v_real:] = np.nan
+    x[2, 3] = -np.inf  # a -inf column: p = 0, 0 log 0 = 0
+    tgt = rng.integers(0, v_real, size=n).astype(np.int32)
+    tgt[4] = IGNORE
+    mask = np.ones(n, dtype=np.uint8)
+    mask[1] = 0
+    g, gl, gh = rng.normal(size=n), rng.normal(size=n), rng.normal(size=n)
+    _, lse, _, _ = o.fwd(x, tgt, mask, real_vocab=v_real)
+    ent = o.entropy(x, real_vocab=v_real)
+    xt = torch.from_numpy(x[:, :v_real].copy()).requires_grad_(True)
+    lsm = torch.log_softmax(xt, dim=1)
+    act = torch.from_numpy((mask != 0) & (tgt != IGNORE))
+    tsafe = torch.from_numpy(np.where(tgt == IGNORE, 0, tgt).astype(np.int64))
+    logp = lsm.gather(1, tsafe[:, None])[:, 0] * act
+    p = lsm.exp()
+    h = -(p * torch.where(p > 0, lsm, torch.zeros_like(lsm))).sum(1)  # 0 log 0 = 0
+    for use_g, use_gl, use_gh in ((1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 1, 1)):
+        xt.grad = None
+        f = (torch.from_numpy(g) * logp * use_g).sum() + (torch.from_numpy(gl) * torch.logsumexp(
+            xt, 1) * use_gl).sum() + (torch.from_numpy(gh) * h * use_gh).sum()
+        f.backward(retain_graph=True)
+        d = o.bwd_ex(x, tgt, mask, lse, real_vocab=v_real, padded_vocab=v_pad, ent=ent,
+                     g=g if use_g else None, g_lse=gl if use_gl else None,
+                     g_ent=gh if use_gh else None)
+        close(d[:, :v_real], xt.grad.numpy(), 1e-10)
+        assert (d[:, v_real:] == 0).all()
+    # with only g it is the plain backward
+    d0 = o.bwd_ex(x, tgt, mask, lse, real_vocab=v_real, padded_vocab=v_pad, g=g)
+    close(d0, o.bwd(x, tgt, mask, lse, g, real_vocab=v_real, padded_vocab=v_pad), 0.0)
+    # brute force on tiny bf16 rows
+    for v in (2, 5, 9):
+        bits = random_bf16(rng, (3, v))
+        xb = decode(bits)
+        t3 = rng.integers(0, v, size=3).astype(np.int32)
+        m3 = np.array([1, 0, 1], dtype=np.uint8)
+        g3, gl3, gh3 = rng.normal(size=3), rng.normal(size=3), rng.normal(size=3)
+        _, l3, _, _ = o.fwd(bits, t3, m3, real_vocab=v)
+        e3 = o.entropy(bits, real_vocab=v)
+        got = o.bwd_ex(bits, t3, m3, l3, real_vocab=v, padded_vocab=v + 3, ent=e3, g=g3,
+                       g_lse=gl3, g_ent=gh3)
+        want = brute.bwd_ex([list(r) for r in xb], t3, m3, g3, gl3, gh3, v, v + 3)
+        close(got, want, 1e-12)
+    # central differences of the oracle's own LSE and entropy
+    eps = 1e-6
+    for r, j in ((0, 0), (3, 11), (6, v_real - 1)):
+        xp, xm = x.copy(), x.copy()
+        xp[r, j] += eps
+        xm[r, j] -= eps
+        dl = (o.fwd(xp, tgt, mask, real_vocab=v_real)[1][r]
+              - o.fwd(xm, tgt, mask, real_vocab=v_real)[1][r]) / (2 * eps)
+        dh = (o.entropy(xp, real_vocab=v_real)[r] - o.entropy(xm, real_vocab=v_real)[r]) / (2 * eps)
+        one = np.zeros(n)
+        one[r] = 1.0
+        got_l = o.bwd_ex(x, tgt, mask, lse, real_vocab=v_real, padded_vocab=v_pad, g_lse=one)
+        got_h = o.bwd_ex(x, tgt, mask, lse, real_vocab=v_real, padded_vocab=v_pad, ent=ent,
+                         g_ent=one)
+        close(got_l[r, j], dl, 1e-6)
+        close(got_h[r, j], dh, 1e-6)
+    # inactive rows get the LSE and entropy terms but no logp term
+    d1 = o.bwd_ex(x, tgt, mask, lse, real_vocab=v_real, padded_vocab=v_pad, g=g)
+    assert (d1[1] == 0).all() and (d1[4] == 0).all()
+
+
+def pin_entropy_partials(o):
+    rng = np.random.default_rng(41)
+    for v_real, v_pad, t in ((5, 5, 2), (3, 8, 4), (100, 128, 8), (17, 24, 5)):
+        bits = random_bf16(rng, (3, v_pad))
+        bits[1, :2] = 0xFF80  # -inf columns
+        x = decode(bits)
+        b = o.tile_bounds(v_pad, t)
+        _, _, pe = o.tile_partials(bits, real_vocab=v_real, padded_vocab=v_pad, num_tiles=t,
+                                   with_entropy=True)
+        for r in range(3):
+            close(pe[r], brute.entropy_partials(list(x[r]), list(b), v_real), 1e-12)
+
+
 PINS = [pin_bf16_decode, pin_geometry, pin_fwd_brute, pin_closed_forms, pin_library,
-        pin_gradient, pin_partials, pin_errors_and_nonfinite, pin_padding_and_ld, pin_lmhead]
+        pin_gradient, pin_partials, pin_errors_and_nonfinite, pin_padding_and_ld, pin_lmhead,
+        pin_entropy, pin_gradient_ex, pin_entropy_partials]
 
 
 @pytest.fixture(scope="module")
@@ -359,12 +481,22 @@ MUTANTS = {
                          "bounds[t] = (padded_vocab / (int64_t)num_tiles) * (int64_t)t;"),
     "onehot_dropped": ("double onehot = (j == (int64_t)t) ? 1.0 : 0.0;",
                        "double onehot = 0.0;"),
-    "identity_partial_wrong": ("double m = -INFINITY, s = 0.0;", "double m = -INFINITY, s = 1.0;"),
+    "identity_partial_wrong": ("double m = -INFINITY, s = 0.0, a = 0.0;",
+                               "double m = -INFINITY, s = 1.0, a = 0.0;"),
     "lse_unshifted_max": ("return m + log(sum);", "return log(sum);"),
     "lmhead_dropped_k": ("for (int64_t q = 0; q < jb->k; ++q) acc += hr[q] * wr[q];",
                          "for (int64_t q = 0; q + 1 < jb->k; ++q) acc += hr[q] * wr[q];"),
     "lmhead_wrong_hidden_row": ("const double* hr = jb->hd + r * jb->k;",
                                 "const double* hr = jb->hd + (r > 0 ? r - 1 : r) * jb->k;"),
+    "entropy_sign": ("h -= exp(lp) * lp;", "h += exp(lp) * lp;"),
+    "entropy_grad_without_h": ("v -= gh * p * ((x[j] - lse) + h);", "v -= gh * p * (x[j] - lse);"),
+    "entropy_grad_sign": ("v -= gh * p * ((x[j] - lse) + h);", "v += gh * p * ((x[j] - lse) + h);"),
+    "lse_grad_dropped": ("double v = g * (oh - p) + gl * p;", "double v = g * (oh - p);"),
+    "ex_onehot_dropped": ("const double oh = (j == (int64_t)t) ? 1.0 : 0.0;",
+                          "const double oh = 0.0;"),
+    "ex_logp_term_on_inactive": ("const double g = (act && jb->g) ? jb->g[r] : 0.0;",
+                                 "const double g = jb->g ? jb->g[r] : 0.0;"),
+    "entropy_partial_unshifted": ("a += exp(x[j] - m) * (x[j] - m);", "a += exp(x[j] - m) * x[j];"),
 }
 
 
