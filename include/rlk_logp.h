@@ -13,6 +13,8 @@
  *           and fp32 selected-logprob and fp32 LSE outputs.  The review excerpt
  *           of the op's apply() shows the target-range check on active tokens
  *           and the "non-finite logsumexp on an active row" error.
+ *   [H100V] "H100 canonical TP/CP validation" (docs/usage/h100-matrix-validation.md):
+ *           the RL runs whose log metrics include the mean entropy.
  *   [I323]  Issue #323 "[WS2][Logprob] H100 validation and reproduction guide
  *           for Issue #241 PR1-PR5", "Test Order / 2. Six-Case TP/CP Matrix":
  *           64 vocabulary tiles over a real = padded vocabulary of 151936;
@@ -157,6 +159,52 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
                         const uint8_t* active_mask, const float* lse, const float* grad_logp,
                         void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Extended forward: rlk_logp_fwd plus the per-row entropy of the softmax over
+ * the real vocabulary,
+ *   H_r = -sum_{j < V_real} p_rj log p_rj,  p_rj = exp(x_rj - LSE_r),  0 log 0 = 0.
+ * The pages return the LSE as a direct diagnostic beside the selected logp
+ * ([PR289] walkthrough: forward_with_lse) and their RL runs log the mean
+ * entropy ([H100V] "H100 canonical TP/CP validation", page
+ * docs/usage/h100-matrix-validation.md: log metrics such as mean
+ * loss/entropy).  Each tile also yields sum exp(x - max) (x - max) over its real
+ * columns, merged in the same ascending tile order, so H is bitwise identical
+ * for every num_virtual_shards, and logp and LSE are bitwise those of
+ * rlk_logp_fwd.
+ *   entropy     (device) float [N] out, non-NULL: H_r for every row; NaN where
+ *               LSE is not finite (no distribution, or NaN / +inf logits).
+ *   workspace   >= rlk_logp_ex_workspace_bytes(desc): the layout of
+ *               rlk_logp_workspace_bytes followed by a third [N][T] float array
+ *               (the entropy statistic) at [256 + 2P, 256 + 3P).
+ * Other arguments and errors as for rlk_logp_fwd. */
+size_t rlk_logp_ex_workspace_bytes(const rlk_logp_desc* desc);
+rlk_status rlk_logp_fwd_ex(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                           const uint8_t* active_mask, float* logp, float* lse, float* entropy,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Extended backward: the gradient of a loss that reads logp, LSE and the
+ * entropy H of rlk_logp_fwd_ex,
+ *   dX[r, j] = a_r g_r ([j == target[r]] - p_rj) + gl_r p_rj - gh_r p_rj (log p_rj + H_r)
+ * on the real columns (+0 on padded ones), where g = grad_logp, gl = grad_lse,
+ * gh = grad_ent and a_r is effective-active.  The logp term applies to
+ * effective-active rows only (logp is a constant +0 elsewhere); the LSE and
+ * entropy terms apply to every row, since both outputs are defined on every
+ * row (reading: the pages return the LSE of every row).  A column at -inf
+ * contributes 0 (0 log 0 = 0); a row whose LSE is not finite gets NaN from any
+ * LSE or entropy term that reaches it.  A row that no term reaches is +0 and
+ * its logits are not read.
+ *   lse         (device) float [N]: the forward's LSE.
+ *   entropy     (device) float [N]: the forward's H; needed when grad_ent is
+ *               non-NULL, otherwise unused (may be NULL).
+ *   grad_logp, grad_lse, grad_ent  (device) float [N] each, or NULL for zero;
+ *               at least one must be given.  With grad_lse and grad_ent both
+ *               NULL the result is bitwise rlk_logp_bwd's.
+ *   other arguments, dlogits layout and errors as for rlk_logp_bwd. */
+rlk_status rlk_logp_bwd_ex(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                           const uint8_t* active_mask, const float* lse, const float* entropy,
+                           const float* grad_logp, const float* grad_lse, const float* grad_ent,
+                           void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward and backward in one launch, for a caller that has the upstream
  * gradient g before the forward (for instance a policy-gradient loss whose

@@ -94,3 +94,40 @@ def check_bwd(d_g: np.ndarray, d_o: np.ndarray, active: np.ndarray, real_vocab: 
             bad = ~(err <= TOL_D32)
         assert not bad.any(), f"{tag}: dlogits max err {np.nanmax(err):.3e} at {np.argwhere(bad)[:3]}"
     return float(err.max(initial=0.0))
+
+
+TOL_ENT = 1e-4
+
+
+def check_entropy(ent_g, ent_o, tag=""):
+    """Entropy on every row: |gpu - oracle| <= 1e-4; NaN exactly where the oracle has NaN."""
+    eg = np.asarray(ent_g, dtype=np.float32).astype(np.float64)
+    eo = np.asarray(ent_o, dtype=np.float64)
+    assert np.array_equal(np.isnan(eg), np.isnan(eo)), f"{tag}: entropy NaN rows differ"
+    fin = ~np.isnan(eo)
+    e = np.abs(eg[fin] - eo[fin])
+    assert e.size == 0 or e.max() <= TOL_ENT, f"{tag}: entropy max err {e.max():.3e}"
+    return float(e.max(initial=0.0))
+
+
+def check_bwd_ex(d_g: np.ndarray, d_o: np.ndarray, zero_rows: np.ndarray, real_vocab: int,
+                 bf16: bool, tag="", raw: np.ndarray | None = None):
+    """The extended backward: rows no term reaches and padded columns are +0 bit for
+    bit; every other element within the dlogits tolerance, NaN where the oracle has
+    NaN (a bad target)."""
+    assert d_g.shape == d_o.shape
+    if raw is not None:
+        assert (raw[zero_rows] == 0).all(), f"{tag}: unreached dlogits row not +0"
+        assert (raw[:, real_vocab:] == 0).all(), f"{tag}: padded dlogits column not +0"
+    rows = ~zero_rows
+    g, o = d_g[rows], d_o[rows]
+    with np.errstate(invalid="ignore"):
+        assert np.array_equal(np.isnan(g), np.isnan(o)), f"{tag}: NaN pattern differs"
+        fin = ~np.isnan(o)
+        err = np.abs(g[fin] - o[fin])
+        if bf16:
+            bad = ~(err <= np.maximum(TOL_D16, bf16_spacing(o[fin])))
+        else:
+            bad = ~(err <= TOL_D32)
+        assert not bad.any(), f"{tag}: dlogits max err {np.nanmax(err):.3e}"
+    return float(err.max(initial=0.0))

@@ -281,3 +281,43 @@ def test_fwd_bwd_host_validation():
     # an empty batch is a no-op
     rlk.rlk_logp_fwd_bwd(desc(num_tokens=0), None, None, None, None, None, None, None, 1024, f32,
                          None, stream=s)
+
+
+def test_extended_forward_and_backward_host_validation():
+    a = _FakeTensor(0x10000000)
+    s = _NoStream()
+    d = desc(num_tokens=32, num_vocab_tiles=64)
+    part = (32 * 64 * 4 + 255) // 256 * 256
+    assert rlk.rlk_logp_ex_workspace_bytes(d) == 256 + 3 * part
+    assert rlk.rlk_logp_ex_workspace_bytes(desc(num_vocab_tiles=0)) == 0
+    need = 256 + 3 * part
+    ws = _FakeTensor(0x20000000, need)
+
+    def fwd(dd=d, ent=a, w=ws, logits=a):
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_fwd_ex(dd, logits, a, None, a, a, ent, w, stream=s)
+        return ei.value.status
+
+    assert fwd(ent=None) == rlk.RLK_ERR_NULL_POINTER
+    assert fwd(w=_FakeTensor(0x20000000, 256 + 2 * part)) == rlk.RLK_ERR_WORKSPACE
+    assert fwd(logits=_FakeTensor(0x10000004)) == rlk.RLK_ERR_ALIGNMENT
+    assert fwd(ent=_FakeTensor(0x10000002)) == rlk.RLK_ERR_ALIGNMENT
+    for kw, code in BAD_DESCS:
+        assert fwd(dd=desc(**kw)) == code, kw
+    f32 = rlk.RLK_DTYPE_F32
+    w256 = _FakeTensor(0x20000000, 256)
+
+    def bwd(ent=a, g=a, gl=None, gh=None, dt=f32, ld_d=1024):
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_bwd_ex(d, a, a, None, a, ent, g, gl, gh, a, ld_d, dt, w256, stream=s)
+        return ei.value.status
+
+    assert bwd(g=None) == rlk.RLK_ERR_NULL_POINTER  # no gradient at all
+    assert bwd(ent=None, gh=a) == rlk.RLK_ERR_NULL_POINTER  # grad_ent needs entropy
+    assert bwd(dt=3) == rlk.RLK_ERR_DTYPE
+    assert bwd(ld_d=1020) == rlk.RLK_ERR_BAD_SHAPE
+    assert bwd(gl=_FakeTensor(0x10000001)) == rlk.RLK_ERR_ALIGNMENT
+    # empty batches are no-ops
+    rlk.rlk_logp_fwd_ex(desc(num_tokens=0), None, None, None, None, None, None, None, stream=s)
+    rlk.rlk_logp_bwd_ex(desc(num_tokens=0), None, None, None, None, None, None, None, None, None,
+                        1024, f32, None, stream=s)

@@ -35,6 +35,7 @@ RLK_DTYPE_BF16 = 1
 RLK_FLAG_VALIDATE = 1
 
 EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd",
+            "rlk_logp_ex_workspace_bytes", "rlk_logp_fwd_ex", "rlk_logp_bwd_ex",
             "rlk_logp_fwd_bwd_workspace_bytes", "rlk_logp_fwd_bwd",
             "rlk_logp_fused_lmhead_workspace_bytes", "rlk_logp_fused_lmhead",
             "rlk_logp_tile_geometry", "rlk_status_string", "rlk_last_error_detail")
@@ -67,6 +68,13 @@ def _load() -> ctypes.CDLL:
     lib.rlk_logp_fwd.restype = ctypes.c_int
     lib.rlk_logp_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz, vp]
     lib.rlk_logp_bwd.restype = ctypes.c_int
+    lib.rlk_logp_ex_workspace_bytes.argtypes = [dp]
+    lib.rlk_logp_ex_workspace_bytes.restype = sz
+    lib.rlk_logp_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_fwd_ex.restype = ctypes.c_int
+    lib.rlk_logp_bwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp,
+                                    sz, vp]
+    lib.rlk_logp_bwd_ex.restype = ctypes.c_int
     lib.rlk_logp_fwd_bwd_workspace_bytes.argtypes = [dp]
     lib.rlk_logp_fwd_bwd_workspace_bytes.restype = sz
     lib.rlk_logp_fwd_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz,
@@ -128,6 +136,28 @@ def rlk_logp_bwd(desc, logits, targets, active_mask, lse, grad_logp, dlogits, ld
     _check(_lib.rlk_logp_bwd(ctypes.byref(desc), _ptr(logits), _ptr(targets), _ptr(active_mask),
                              _ptr(lse), _ptr(grad_logp), _ptr(dlogits), ld_dlogits,
                              dlogits_dtype, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_ex_workspace_bytes(desc: rlk_logp_desc) -> int:
+    return int(_lib.rlk_logp_ex_workspace_bytes(ctypes.byref(desc)))
+
+
+def rlk_logp_fwd_ex(desc, logits, targets, active_mask, logp, lse, entropy, workspace,
+                    stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_fwd_ex(ctypes.byref(desc), _ptr(logits), _ptr(targets),
+                                _ptr(active_mask), _ptr(logp), _ptr(lse), _ptr(entropy),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_bwd_ex(desc, logits, targets, active_mask, lse, entropy, grad_logp, grad_lse,
+                    grad_ent, dlogits, ld_dlogits: int, dlogits_dtype: int, workspace,
+                    stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_bwd_ex(ctypes.byref(desc), _ptr(logits), _ptr(targets),
+                                _ptr(active_mask), _ptr(lse), _ptr(entropy), _ptr(grad_logp),
+                                _ptr(grad_lse), _ptr(grad_ent), _ptr(dlogits), ld_dlogits,
+                                dlogits_dtype, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def rlk_logp_fwd_bwd_workspace_bytes(desc: rlk_logp_desc) -> int:
@@ -223,6 +253,103 @@ def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torc
     rlk_logp_bwd(desc, logits, targets, _u8_mask(active_mask), lse, grad_logp, dl, ld_d, code,
                  workspace, stream)
     return dl[:, :v_pad]
+
+
+def forward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *,
+               real_vocab: int, padded_vocab: int | None = None, num_vocab_tiles: int = 64,
+               num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
+               workspace: torch.Tensor | None = None, stream=None):
+    """(logp, lse, entropy), fp32 [N] each."""
+    n = logits.shape[0]
+    desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
+                     num_vocab_tiles, num_virtual_shards, ignore_index, validate)
+    logp = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+    ent = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if workspace is None:
+        nbytes = rlk_logp_ex_workspace_bytes(desc)
+        if nbytes == 0:
+            raise ValueError(f"invalid rlk_logp_desc: {rlk_last_error_detail()}")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
+    rlk_logp_fwd_ex(desc, logits, targets, _u8_mask(active_mask), logp, lse, ent, workspace,
+                    stream)
+    return logp, lse, ent
+
+
+def backward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torch.Tensor,
+                entropy=None, grad_logp=None, grad_lse=None, grad_ent=None, *, real_vocab: int,
+                padded_vocab: int | None = None, out_dtype=torch.float32,
+                ignore_index: int = -100, validate: bool = False,
+                num_vocab_tiles: int | None = None, workspace: torch.Tensor | None = None,
+                stream=None):
+    """dlogits [N, V_pad] of a loss on (logp, lse, entropy); absent gradients are zero."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    n = logits.shape[0]
+    v_pad = padded_vocab or logits.shape[1]
+    tiles = num_vocab_tiles if num_vocab_tiles is not None else min(64, v_pad)
+    desc = make_desc(n, real_vocab, v_pad, logits.stride(0), tiles, 1, ignore_index, validate)
+    ld_d = (v_pad + 7) // 8 * 8
+    dl = torch.empty((n, ld_d), dtype=out_dtype, device=logits.device)
+    if workspace is None:
+        workspace = workspace_for(desc, logits.device)
+    code = RLK_DTYPE_BF16 if out_dtype == torch.bfloat16 else RLK_DTYPE_F32
+    rlk_logp_bwd_ex(desc, logits, targets, _u8_mask(active_mask), lse, entropy, grad_logp,
+                    grad_lse, grad_ent, dl, ld_d, code, workspace, stream)
+    return dl[:, :v_pad]
+
+
+class _SelectedTokenLogprob(torch.autograd.Function):
+    """(logp, lse, entropy) of bf16 logits, differentiable in all three; the forward
+    and the backward are rlk_logp_fwd_ex and rlk_logp_bwd_ex."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, active_mask, real_vocab, padded_vocab, num_vocab_tiles,
+                ignore_index):
+        logp, lse, ent = forward_ex(logits, targets, active_mask, real_vocab=real_vocab,
+                                    padded_vocab=padded_vocab, num_vocab_tiles=num_vocab_tiles,
+                                    ignore_index=ignore_index)
+        ctx.save_for_backward(logits, targets, lse, ent)
+        ctx.active_mask = active_mask
+        ctx.cfg = (real_vocab, padded_vocab, num_vocab_tiles, ignore_index)
+        return logp, lse, ent
+
+    @staticmethod
+    def backward(ctx, g_logp, g_lse, g_ent):
+        logits, targets, lse, ent = ctx.saved_tensors
+        real_vocab, padded_vocab, num_vocab_tiles, ignore_index = ctx.cfg
+
+        def vec(t):
+            return None if t is None else t.contiguous().float()
+        g_logp, g_lse, g_ent = vec(g_logp), vec(g_lse), vec(g_ent)
+        if g_logp is None and g_lse is None and g_ent is None:
+            return (None,) * 7
+        v_pad = padded_vocab or logits.shape[1]
+        d = backward_ex(logits, targets, ctx.active_mask, lse, ent, g_logp, g_lse, g_ent,
+                        real_vocab=real_vocab, padded_vocab=v_pad, out_dtype=logits.dtype,
+                        ignore_index=ignore_index, num_vocab_tiles=num_vocab_tiles)
+        if d.shape == logits.shape and d.is_contiguous():
+            grad = d
+        else:
+            grad = torch.zeros_like(logits)
+            grad[:, :v_pad] = d
+        return grad, None, None, None, None, None, None
+
+
+def selected_token_logprob(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *,
+                           real_vocab: int, padded_vocab: int | None = None,
+                           num_vocab_tiles: int = 64, ignore_index: int = -100):
+    """The op as a differentiable torch function: returns (logp, lse, entropy), fp32 [N].
+
+    This is the interface a loss built on the selected-token log-probability
+    consumes (a policy-gradient loss on logp, a penalty on LSE, an entropy bonus):
+    autograd hands the three upstream gradients to rlk_logp_bwd_ex.  logits is
+    bf16 [N, ld] with unit column stride; its gradient has its dtype.
+    """
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.dtype != torch.bfloat16:
+        raise ValueError("logits must be a 2-D bf16 tensor with unit column stride")
+    return _SelectedTokenLogprob.apply(logits, targets, active_mask, real_vocab, padded_vocab,
+                                       num_vocab_tiles, ignore_index)
 
 
 def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,

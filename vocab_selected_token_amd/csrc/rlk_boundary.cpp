@@ -83,6 +83,9 @@ size_t partial_bytes(const rlk_logp_desc* d) {
 
 size_t needed_workspace(const rlk_logp_desc* d) { return kStatusBytes + 2 * partial_bytes(d); }
 
+// The extended forward adds a third [N][T] array (the entropy statistic).
+size_t needed_workspace_ex(const rlk_logp_desc* d) { return kStatusBytes + 3 * partial_bytes(d); }
+
 rlk_status hip_fail(hipError_t e, const char* what) {
   return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -134,23 +137,29 @@ rlk_status rlk_logp_tile_geometry(int64_t padded_vocab, int32_t num_vocab_tiles,
   return ok();
 }
 
-rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
-                        const uint8_t* active_mask, float* logp, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream_ptr) {
+}  // extern "C"
+
+namespace {
+
+// The forward of rlk_logp_fwd and rlk_logp_fwd_ex (entropy != null: the
+// entropy statistic rides along in stage 1 and stage 2 merges it).
+rlk_status run_forward(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                       const uint8_t* active_mask, float* logp, float* lse, float* entropy,
+                       void* workspace, size_t workspace_bytes, void* stream_ptr) {
   rlk_status st = check_desc(desc);
   if (st != RLK_OK) return st;
   const int64_t n = desc->num_tokens;
   if (n == 0) return ok();
   if (!logits || !targets || !logp || !lse)
     return fail(RLK_ERR_NULL_POINTER, "logits, targets, logp and lse must be non-NULL");
+  const size_t need = entropy ? needed_workspace_ex(desc) : needed_workspace(desc);
   if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
-  if (workspace_bytes < needed_workspace(desc))
-    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes,
-                needed_workspace(desc));
+  if (workspace_bytes < need)
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
   if (!aligned(logits, 16)) return fail(RLK_ERR_ALIGNMENT, "logits not 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
-  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4))
-    return fail(RLK_ERR_ALIGNMENT, "targets, logp and lse must be 4-byte aligned");
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) || !aligned(entropy, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, logp, lse and entropy must be 4-byte aligned");
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   const int32_t T = desc->num_vocab_tiles, S = desc->num_virtual_shards;
@@ -158,6 +167,8 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
   uint32_t* status = reinterpret_cast<uint32_t*>(ws);
   float* pmax = reinterpret_cast<float*>(ws + kStatusBytes);
   float* psum = reinterpret_cast<float*>(ws + kStatusBytes + partial_bytes(desc));
+  float* pent =
+      entropy ? reinterpret_cast<float*>(ws + kStatusBytes + 2 * partial_bytes(desc)) : nullptr;
   const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
 
   hipError_t e;
@@ -175,6 +186,7 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
   a1.tile_width = (desc->padded_vocab % T == 0) ? (int32_t)(desc->padded_vocab / T) : 0;
   a1.pmax = pmax;
   a1.psum = psum;
+  a1.pent = pent;
   for (int32_t s = 0; s < S; ++s) {  // one launch per virtual shard
     const int32_t t0 = (int32_t)(((int64_t)s * T) / S);
     const int32_t t1 = (int32_t)(((int64_t)(s + 1) * T) / S);
@@ -194,11 +206,13 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
   a2.num_tiles = T;
   a2.pmax = pmax;
   a2.psum = psum;
+  a2.pent = pent;
   a2.targets = targets;
   a2.mask = active_mask;
   a2.ignore_index = desc->ignore_index;
   a2.logp = logp;
   a2.lse = lse;
+  a2.entropy = entropy;
   a2.status = status;
   e = rlk::launch_stage2(a2, stream);
   if (e != hipSuccess) return hip_fail(e, "stage2_merge launch");
@@ -206,10 +220,45 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
   return ok();
 }
 
-rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
-                        const uint8_t* active_mask, const float* lse, const float* grad_logp,
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, float* logp, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream_ptr) {
+  return run_forward(desc, logits, targets, active_mask, logp, lse, nullptr, workspace,
+                     workspace_bytes, stream_ptr);
+}
+
+size_t rlk_logp_ex_workspace_bytes(const rlk_logp_desc* desc) {
+  if (check_desc(desc) != RLK_OK) return 0;
+  return needed_workspace_ex(desc);
+}
+
+rlk_status rlk_logp_fwd_ex(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                           const uint8_t* active_mask, float* logp, float* lse, float* entropy,
+                           void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_desc(desc);
+  if (st != RLK_OK) return st;
+  if (desc->num_tokens > 0 && !entropy)
+    return fail(RLK_ERR_NULL_POINTER, "entropy must be non-NULL (rlk_logp_fwd has no entropy)");
+  return run_forward(desc, logits, targets, active_mask, logp, lse, entropy, workspace,
+                     workspace_bytes, stream_ptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward of rlk_logp_bwd and rlk_logp_bwd_ex.  With grad_lse and
+// grad_ent both null the plain kernel runs, so rlk_logp_bwd_ex without the
+// extra gradients gives rlk_logp_bwd's bits.
+rlk_status run_backward(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, const float* lse, const float* entropy,
+                        const float* grad_logp, const float* grad_lse, const float* grad_ent,
                         void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
-                        void* workspace, size_t workspace_bytes, void* stream_ptr) {
+                        void* workspace, size_t workspace_bytes, void* stream_ptr, bool ex) {
   rlk_status st = check_desc(desc);
   if (st != RLK_OK) return st;
   if (dlogits_dtype != RLK_DTYPE_F32 && dlogits_dtype != RLK_DTYPE_BF16)
@@ -223,17 +272,29 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
                 (long long)ld_dlogits);
   const int64_t n = desc->num_tokens;
   if (n == 0) return ok();
-  if (!logits || !targets || !lse || !grad_logp || !dlogits)
-    return fail(RLK_ERR_NULL_POINTER, "logits, targets, lse, grad_logp and dlogits must be "
-                                      "non-NULL");
+  if (!ex) {
+    if (!logits || !targets || !lse || !grad_logp || !dlogits)
+      return fail(RLK_ERR_NULL_POINTER, "logits, targets, lse, grad_logp and dlogits must be "
+                                        "non-NULL");
+  } else {
+    if (!logits || !targets || !lse || !dlogits)
+      return fail(RLK_ERR_NULL_POINTER, "logits, targets, lse and dlogits must be non-NULL");
+    if (!grad_logp && !grad_lse && !grad_ent)
+      return fail(RLK_ERR_NULL_POINTER, "at least one of grad_logp, grad_lse and grad_ent must "
+                                        "be non-NULL");
+    if (grad_ent && !entropy)
+      return fail(RLK_ERR_NULL_POINTER, "grad_ent needs the forward's entropy");
+  }
   if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
   if (workspace_bytes < kStatusBytes)
     return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < %zu", workspace_bytes, kStatusBytes);
   if (!aligned(logits, 16) || !aligned(dlogits, 16))
     return fail(RLK_ERR_ALIGNMENT, "logits and dlogits must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
-  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4))
-    return fail(RLK_ERR_ALIGNMENT, "targets, lse and grad_logp must be 4-byte aligned");
+  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4) ||
+      !aligned(grad_lse, 4) || !aligned(grad_ent, 4) || !aligned(entropy, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, lse, entropy and the gradients must be 4-byte "
+                                   "aligned");
   if (n * rlk::bwd_col_blocks((int32_t)desc->padded_vocab) > kI32Max)
     return fail(RLK_ERR_BAD_SHAPE, "num_tokens * column blocks too large for one launch");
 
@@ -256,14 +317,40 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
   a.ignore_index = desc->ignore_index;
   a.lse = lse;
   a.grad = grad_logp;
+  a.grad_lse = grad_lse;
+  a.grad_ent = grad_ent;
+  a.entropy = entropy;
   a.dlogits = dlogits;
   a.ld_d = ld_dlogits;
   a.out_bf16 = dlogits_dtype == RLK_DTYPE_BF16;
   a.status = status;
-  e = rlk::launch_bwd(a, stream);
+  e = rlk::launch_bwd(a, stream);  // the plain kernel unless grad_lse or grad_ent is given
   if (e != hipSuccess) return hip_fail(e, "bwd_dlogits launch");
   if (validate) return finish_validate(status, stream, false);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                        const uint8_t* active_mask, const float* lse, const float* grad_logp,
+                        void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  return run_backward(desc, logits, targets, active_mask, lse, nullptr, grad_logp, nullptr,
+                      nullptr, dlogits, ld_dlogits, dlogits_dtype, workspace, workspace_bytes,
+                      stream_ptr, false);
+}
+
+rlk_status rlk_logp_bwd_ex(const rlk_logp_desc* desc, const void* logits, const int32_t* targets,
+                           const uint8_t* active_mask, const float* lse, const float* entropy,
+                           const float* grad_logp, const float* grad_lse, const float* grad_ent,
+                           void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  return run_backward(desc, logits, targets, active_mask, lse, entropy, grad_logp, grad_lse,
+                      grad_ent, dlogits, ld_dlogits, dlogits_dtype, workspace, workspace_bytes,
+                      stream_ptr, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,11 +559,13 @@ rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
   a2.num_tiles = desc->num_vocab_tiles;
   a2.pmax = a.pmax;
   a2.psum = a.psum;
+  a2.pent = nullptr;
   a2.targets = targets;
   a2.mask = active_mask;
   a2.ignore_index = desc->ignore_index;
   a2.logp = logp;
   a2.lse = lse;
+  a2.entropy = nullptr;
   a2.status = status;
   e = rlk::launch_stage2(a2, stream);
   if (e != hipSuccess) return hip_fail(e, "stage2_merge launch");

@@ -20,6 +20,7 @@ struct Stage1Args {
   int32_t tile_count;
   float* pmax;  // [num_rows][num_tiles]
   float* psum;
+  float* pent;  // entropy statistic [num_rows][num_tiles], or null
 };
 
 struct Stage2Args {
@@ -31,11 +32,13 @@ struct Stage2Args {
   int32_t num_tiles;
   const float* pmax;
   const float* psum;
+  const float* pent;  // with entropy: the stage-1 entropy statistic
   const int32_t* targets;
   const uint8_t* mask;  // may be null
   int32_t ignore_index;
   float* logp;
   float* lse;
+  float* entropy;  // per-row entropy out, or null
   uint32_t* status;
 };
 
@@ -49,7 +52,10 @@ struct BwdArgs {
   const uint8_t* mask;  // may be null
   int32_t ignore_index;
   const float* lse;
-  const float* grad;
+  const float* grad;      // may be null with grad_lse or grad_ent given
+  const float* grad_lse;  // null = zero
+  const float* grad_ent;  // null = zero
+  const float* entropy;   // read where grad_ent is nonzero
   void* dlogits;
   int64_t ld_d;
   bool out_bf16;

@@ -2,11 +2,15 @@
 //
 // Three kernels, one per step of the path:
 //   stage1_partials  per (row, vocab tile) fp32 (max, sumexp) over the tile's
-//                    real columns ("masked per-tile partials").
+//                    real columns ("masked per-tile partials"); optionally the
+//                    entropy statistic sum exp(x - max) (x - max) as well.
 //   stage2_merge     per row: merge the T partials in ascending tile order into
-//                    LSE, gather the target logit, apply the active mask and
-//                    ignore_index, flag bad targets / non-finite LSE.
-//   bwd_dlogits      dX = g * (onehot - exp(X - LSE)) on effective-active rows.
+//                    LSE (and the entropy H), gather the target logit, apply the
+//                    active mask and ignore_index, flag bad targets / non-finite
+//                    LSE.
+//   bwd_dlogits      dX = g * (onehot - exp(X - LSE)) on effective-active rows;
+//                    optionally plus the LSE and entropy gradients.
+// plus fwd_bwd_rows, all three in one launch when g is known up front.
 //
 // Sources (web pages, by title and section): PR #289 "[WS2][PR4][Logp] feat:
 // add distributed TP/CP logprob drift report", stacked PR1 commit messages
@@ -95,22 +99,36 @@ __device__ __forceinline__ float row_ror(float v) {
 
 // Fold 8 unpacked values into a lane's running (m, s) pair; the values are a
 // pass of kChunks*8 columns held in registers (max first, then the sum).
-template <int NV>
-__device__ __forceinline__ void fold_values(const float (&v)[NV], float& m, float& s) {
+//
+// With kEnt the lane also keeps a = sum exp(x - m) (x - m), the entropy's
+// statistic relative to the running max: when the max moves from m to nm,
+// a becomes (a + (m - nm) s) exp(m - nm).  A column at -inf adds exp(-inf) = 0
+// to s and, through the clamp of x - m to -FLT_MAX, exactly 0 to a.  The (m, s)
+// arithmetic is the same with or without kEnt.
+template <int NV, bool kEnt = false>
+__device__ __forceinline__ void fold_values(const float (&v)[NV], float& m, float& s, float& a) {
   float bm = v[0];
 #pragma unroll
   for (int i = 1; i < NV; ++i) bm = maxnan(bm, v[i]);
   const float nm = maxnan(m, bm);
   if (nm == kNegInf) return;  // everything so far is -inf: (m, s) stays (-inf, 0)
   // rescale the running sum to the new max (exp2(0) == 1 leaves it unchanged)
-  s = s * exp2_hw((m - nm) * kLog2e);
+  const float r = exp2_hw((m - nm) * kLog2e);
+  if (kEnt) a = (m == kNegInf) ? 0.0f : (a + (m - nm) * s) * r;
+  s = s * r;
   const float nml = nm;
 #pragma unroll
   for (int c = 0; c < NV / 8; ++c) {
-    float cs = 0.0f;
+    float cs = 0.0f, ca = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cs += exp2_hw((v[c * 8 + e] - nml) * kLog2e);
+    for (int e = 0; e < 8; ++e) {
+      const float t = v[c * 8 + e] - nml;
+      const float ex = exp2_hw(t * kLog2e);
+      cs += ex;
+      if (kEnt) ca = fmaf(ex, __builtin_fmaxf(t, -__FLT_MAX__), ca);
+    }
     s += cs;
+    if (kEnt) a += ca;
   }
   m = nm;
 }
@@ -136,8 +154,9 @@ __device__ __forceinline__ void load_pass(uint4 (&q)[kChunks], const uint4* __re
   }
 }
 
+template <bool kEnt>
 __device__ __forceinline__ void fold_pass(const uint4 (&q)[kChunks], int32_t b, int32_t lo_c,
-                                          int32_t hi_c, int gl, float& m, float& s) {
+                                          int32_t hi_c, int gl, float& m, float& s, float& a) {
   float v[kChunks * 8];
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
@@ -147,7 +166,7 @@ __device__ __forceinline__ void fold_pass(const uint4 (&q)[kChunks], int32_t b, 
       w = make_uint4(kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair);
     unpack8(w, &v[k * 8]);
   }
-  fold_values(v, m, s);
+  fold_values<kChunks * 8, kEnt>(v, m, s, a);
 }
 
 // Columns [lo, hi) of tile `tile`: floor(t * V_pad / T) bounds (tile_width =
@@ -180,12 +199,15 @@ __device__ __forceinline__ void tile_range(int32_t tile, int32_t tile_width, int
 //      chunks are masked (leading and trailing passes);
 //   3. the 16 lanes combined by an exact max and a fixed rotate tree.
 // kNt selects the nontemporal load hint and kDepth the number of passes whose
-// loads are in flight (1 or 2); neither changes the arithmetic.
-template <bool kNt, int kDepth>
+// loads are in flight (1 or 2); neither changes the arithmetic.  With kEnt the
+// group also returns la = sum exp(x - gm) (x - gm) over the tile (0 for the
+// identity partial); gm and ls are the same bits with or without it.
+template <bool kNt, int kDepth, bool kEnt = false>
 __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int32_t lo,
-                                             int32_t hi, int gl, float& gm_out, float& ls_out) {
+                                             int32_t hi, int gl, float& gm_out, float& ls_out,
+                                             float& la_out) {
   static_assert(kDepth == 1 || kDepth == 2, "prefetch depth is 1 or 2 passes");
-  float m = kNegInf, s = 0.0f;
+  float m = kNegInf, s = 0.0f, a = 0.0f;
   const int32_t cf_lo = (lo + 7) >> 3;  // first full chunk
   int32_t cf_hi = hi >> 3;              // end of full chunks
   if (cf_hi < cf_lo) cf_hi = cf_lo;
@@ -211,24 +233,24 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < e_lo || e >= e_hi) v[e] = kNegInf;
-      fold_values(v, m, s);
+      fold_values<8, kEnt>(v, m, s, a);
     }
   }
   if (kDepth == 1) {
     for (int32_t p = 0; p < npass; ++p) {
       const int32_t b = base0 + p * kPassChunks;
       load_pass<kNt>(qa, rowp, b, cf_lo, cf_hi, gl);
-      fold_pass(qa, b, cf_lo, cf_hi, gl, m, s);
+      fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
     }
   } else {
     // two passes in flight: the next pass's loads are issued before this one folds
     for (int32_t p = 0; p < npass; p += 2) {
       const int32_t b = base0 + p * kPassChunks;
       if (p + 1 < npass) load_pass<kNt>(qb, rowp, b + kPassChunks, cf_lo, cf_hi, gl);
-      fold_pass(qa, b, cf_lo, cf_hi, gl, m, s);
+      fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
       if (p + 1 >= npass) break;
       if (p + 2 < npass) load_pass<kNt>(qa, rowp, b + 2 * kPassChunks, cf_lo, cf_hi, gl);
-      fold_pass(qb, b + kPassChunks, cf_lo, cf_hi, gl, m, s);
+      fold_pass<kEnt>(qb, b + kPassChunks, cf_lo, cf_hi, gl, m, s, a);
     }
   }
 
@@ -237,15 +259,29 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
   gm = maxnan(gm, row_ror<4>(gm));
   gm = maxnan(gm, row_ror<2>(gm));
   gm = maxnan(gm, row_ror<1>(gm));
-  float ls = 0.0f;
-  if (gm != kNegInf && m != kNegInf) ls = s * exp2_hw((m - gm) * kLog2e);
+  float ls = 0.0f, la = 0.0f;
+  if (gm != kNegInf && m != kNegInf) {
+    const float r = exp2_hw((m - gm) * kLog2e);
+    ls = s * r;
+    if (kEnt) la = (a + (m - gm) * s) * r;
+  }
   ls += row_ror<8>(ls);
   ls += row_ror<4>(ls);
   ls += row_ror<2>(ls);
   ls += row_ror<1>(ls);
-  if (gm == kNegInf) ls = 0.0f;  // the (-inf, 0) identity partial
+  if (kEnt) {
+    la += row_ror<8>(la);
+    la += row_ror<4>(la);
+    la += row_ror<2>(la);
+    la += row_ror<1>(la);
+  }
+  if (gm == kNegInf) {  // the (-inf, 0) identity partial
+    ls = 0.0f;
+    la = 0.0f;
+  }
   gm_out = gm;
   ls_out = ls;
+  la_out = la;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,15 +290,18 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
 //   tiles       [tile_begin, tile_begin + tile_count) of T, for every row
 //   tile_width  V_pad / T when T divides V_pad, else 0 (floor formula)
 //   pmax, psum  [N][T] fp32
+//   pent        [N][T] fp32, the entropy statistic (kEnt only)
 // Work item i = row * tile_count + (tile - tile_begin); group q of wave w of
 // work block b (the XCD-local renumbering of blockIdx.x) takes item
 // 16b + 4w + q.  Columns >= V_real never enter the arithmetic; chunks
 // that straddle a tile bound are masked by column index.
 // ---------------------------------------------------------------------------
+template <bool kEnt>
 __global__ __launch_bounds__(256) void stage1_partials(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t tile_begin,
-    int32_t tile_count, float* __restrict__ pmax, float* __restrict__ psum) {
+    int32_t tile_count, float* __restrict__ pmax, float* __restrict__ psum,
+    float* __restrict__ pent) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int gl = lane & 15;
@@ -285,13 +324,14 @@ __global__ __launch_bounds__(256) void stage1_partials(
   if (have) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
   const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
 
-  float gm, ls;
-  tile_partial<true, 2>(rowp, lo, hi, gl, gm, ls);
+  float gm, ls, la;
+  tile_partial<true, 2, kEnt>(rowp, lo, hi, gl, gm, ls, la);
 
   if (have && gl == 0) {
     const int64_t o = (int64_t)row * num_tiles + tile;
     pmax[o] = gm;
     psum[o] = ls;
+    if (kEnt) pent[o] = la;
   }
 }
 
@@ -340,16 +380,53 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
   return M + logf(S);
 }
 
+// merge_row's arithmetic plus the entropy: alongside S it accumulates, in the
+// same ascending order, A = sum_t exp(m_t - M) (a_t + (m_t - M) s_t), which is
+// sum_j exp(x_j - M) (x_j - M) over the row.  Then LSE = M + log S (the same
+// bits as merge_row) and H = log S - A / S; H is NaN where LSE is not finite
+// (no distribution).
+__device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
+                                                   const float* __restrict__ ps,
+                                                   const float* __restrict__ pa,
+                                                   int32_t num_tiles, float& H) {
+  float M = kNegInf;
+  for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
+  H = __builtin_nanf("");
+  if (M == kNegInf) return kNegInf;
+  float S = 0.0f, A = 0.0f;
+  for (int32_t t = 0; t < num_tiles; ++t) {
+    const float mt = pm[t];
+    if (mt != kNegInf) {
+      const float e = expf(mt - M);
+      S = fmaf(ps[t], e, S);
+      A = fmaf(e, fmaf(mt - M, ps[t], pa[t]), A);
+    }
+  }
+  const float lS = logf(S);
+  const float L = M + lS;
+  if (__builtin_isfinite(L)) H = lS - A / S;
+  return L;
+}
+
+template <bool kEnt>
 __global__ __launch_bounds__(kMergeThreads) void stage2_merge(
     const uint16_t* __restrict__ logits, const float* __restrict__ target_logit, int64_t ld,
     int32_t num_rows, int32_t real_vocab,
     int32_t num_tiles, const float* __restrict__ pmax, const float* __restrict__ psum,
-    const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
-    float* __restrict__ logp, float* __restrict__ lse, uint32_t* __restrict__ status) {
+    const float* __restrict__ pent, const int32_t* __restrict__ targets,
+    const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ logp,
+    float* __restrict__ lse, float* __restrict__ entropy, uint32_t* __restrict__ status) {
   const int32_t r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= num_rows) return;
-  const float L = merge_row(pmax + (int64_t)r * num_tiles, psum + (int64_t)r * num_tiles,
-                            num_tiles);
+  float L;
+  if (kEnt) {
+    float H;
+    L = merge_row_entropy(pmax + (int64_t)r * num_tiles, psum + (int64_t)r * num_tiles,
+                          pent + (int64_t)r * num_tiles, num_tiles, H);
+    entropy[r] = H;
+  } else {
+    L = merge_row(pmax + (int64_t)r * num_tiles, psum + (int64_t)r * num_tiles, num_tiles);
+  }
   lse[r] = L;
 
   const bool act = (mask == nullptr || mask[r] != 0);
@@ -455,13 +532,63 @@ __device__ __forceinline__ void dlogits_chunk(const uint4& q, int32_t j0, bool a
   }
 }
 
-template <typename OutT>
+// The extended gradient of the 8 columns [j0, j0 + 8) of one row, with the
+// LSE and entropy terms (the derivatives of LSE and of H = -sum p log p):
+//   d_j = g ([j == t] - p_j) + gl p_j - gh p_j (log p_j + H),  log p_j = x_j - L
+// computed as p_j (w - g) off the target and g (1 - p_t) + p_t w at it, with
+// w = gl - gh (x_j - L + H) (w = gl when gh == 0).  A column at -inf has
+// p = 0 and contributes 0 to every term (0 log 0 = 0).  `need` is false on a
+// row that no term reaches (it stays +0 and is not read); `bad` marks an
+// effective-active row with a target outside [0, V_real) (NaN on its real
+// columns).
+__device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, bool need, bool bad,
+                                                 float L, float g, float gl, float gh, float H,
+                                                 int32_t tgt, int32_t real_vocab,
+                                                 float (&d)[8]) {
+  if (!need) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+  } else if (bad) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
+  } else if (j0 >= real_vocab) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+  } else {
+    float x[8];
+    unpack8(q, x);
+    float p[8], w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = x[e] - L;
+      p[e] = exp2_hw(t * kLog2e);
+      w[e] = gl;
+      if (gh != 0.0f) w[e] = (p[e] == 0.0f) ? 0.0f : gl - gh * (t + H);
+      d[e] = (p[e] == 0.0f) ? 0.0f : p[e] * (w[e] - g);
+    }
+    if (j0 + 8 > real_vocab) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e >= real_vocab) d[e] = 0.0f;
+    }
+    if (tgt >= j0 && tgt < j0 + 8) {
+      const int e = tgt - j0;
+      d[e] = g * (1.0f - p[e]) + p[e] * w[e];
+    }
+  }
+}
+
+// kEx: the extended gradient (grad_lse, grad_ent, entropy may be given; any
+// of grad, grad_lse, grad_ent may be null = zero).  Without kEx the kernel is
+// the plain backward and the extra pointers are unused.
+template <typename OutT, bool kEx>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
     int32_t padded_vocab, int32_t col_blocks, const int32_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, int32_t ignore_index, const float* __restrict__ lse,
-    const float* __restrict__ grad, OutT* __restrict__ dlogits, int64_t ld_d,
-    uint32_t* __restrict__ status) {
+    const float* __restrict__ grad, const float* __restrict__ grad_lse,
+    const float* __restrict__ grad_ent, const float* __restrict__ entropy,
+    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status) {
   const int32_t row = blockIdx.x / col_blocks;
   const int32_t cb = blockIdx.x - row * col_blocks;
   const bool act_mask = (mask == nullptr || mask[row] != 0);
@@ -469,14 +596,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
   const bool act = act_mask && tgt != ignore_index;
   const bool bad = act && (tgt < 0 || tgt >= real_vocab);
   if (bad && cb == 0 && threadIdx.x == 0) status[0] = 1u;
-  const float L = act ? lse[row] : 0.0f;
-  const float g = act ? grad[row] : 0.0f;
+  float gl = 0.0f, gh = 0.0f, H = 0.0f;
+  if (kEx) {
+    gl = grad_lse ? grad_lse[row] : 0.0f;
+    gh = grad_ent ? grad_ent[row] : 0.0f;
+    if (gh != 0.0f) H = entropy[row];
+  }
+  const bool need = act || gl != 0.0f || gh != 0.0f;
+  const float L = need ? lse[row] : 0.0f;
+  const float g = (act && (!kEx || grad)) ? grad[row] : 0.0f;
   OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
   const uint4* __restrict__ xrow = logits + (int64_t)row * ld_chunks;
   const int32_t c0 = cb * (kBwdCols / 8) + threadIdx.x;
 
   uint4 q[kBwdUnroll];
-  if (act && !bad) {
+  if (need && !bad) {
 #pragma unroll
     for (int k = 0; k < kBwdUnroll; ++k) {
       const int32_t c = c0 + k * kBwdThreads;
@@ -489,7 +623,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
     const int32_t j0 = c << 3;
     if (j0 >= padded_vocab) continue;
     float d[8];
-    dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
+    if (kEx)
+      dlogits_chunk_ex(q[k], j0, need, bad, L, g, gl, gh, H, act ? tgt : -1, real_vocab, d);
+    else
+      dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
     Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
   }
 }
@@ -582,8 +719,8 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
     const int32_t tile = t0 + grp;
     int32_t lo = 0, hi = 0;
     if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
-    float gm, ls;
-    tile_partial<false, 1>(rowp, lo, hi, gl, gm, ls);
+    float gm, ls, la;
+    tile_partial<false, 1>(rowp, lo, hi, gl, gm, ls, la);
     if (tile < num_tiles && gl == 0) {
       s_m[tile] = gm;
       s_s[tile] = ls;
@@ -672,21 +809,34 @@ hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_rows * a.tile_count;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)stage1_blocks(items));
-  hipLaunchKernelGGL(stage1_partials, grid, dim3(kWavesPerBlock * 64), 0, stream,
-                     reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
-                     a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
-                     a.tile_count, a.pmax, a.psum);
+  if (a.pent) {
+    hipLaunchKernelGGL(stage1_partials<true>, grid, dim3(kWavesPerBlock * 64), 0, stream,
+                       reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
+                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
+                       a.tile_count, a.pmax, a.psum, a.pent);
+  } else {
+    hipLaunchKernelGGL(stage1_partials<false>, grid, dim3(kWavesPerBlock * 64), 0, stream,
+                       reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
+                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
+                       a.tile_count, a.pmax, a.psum, nullptr);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((a.num_rows + kMergeThreads - 1) / kMergeThreads));
-  hipLaunchKernelGGL(stage2_merge, grid, dim3(kMergeThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
-                     a.num_rows, a.real_vocab,
-                     a.num_tiles, a.pmax, a.psum, a.targets, a.mask, a.ignore_index, a.logp,
-                     a.lse, a.status);
+  if (a.entropy) {
+    hipLaunchKernelGGL(stage2_merge<true>, grid, dim3(kMergeThreads), 0, stream,
+                       reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
+                       a.num_rows, a.real_vocab, a.num_tiles, a.pmax, a.psum, a.pent, a.targets,
+                       a.mask, a.ignore_index, a.logp, a.lse, a.entropy, a.status);
+  } else {
+    hipLaunchKernelGGL(stage2_merge<false>, grid, dim3(kMergeThreads), 0, stream,
+                       reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
+                       a.num_rows, a.real_vocab, a.num_tiles, a.pmax, a.psum, nullptr,
+                       a.targets, a.mask, a.ignore_index, a.logp, a.lse, nullptr, a.status);
+  }
   return hipGetLastError();
 }
 
@@ -699,17 +849,20 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int32_t cbs = (int32_t)bwd_col_blocks(a.padded_vocab);
   const dim3 grid((unsigned)((int64_t)a.num_rows * cbs));
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  const bool ex = a.grad_lse || a.grad_ent;
+#define RLK_LAUNCH_BWD(OUT_T, EX)                                                              \
+  hipLaunchKernelGGL((bwd_dlogits<OUT_T, EX>), grid, dim3(kBwdThreads), 0, stream, x,         \
+                     a.ld / 8, a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets,     \
+                     a.mask, a.ignore_index, a.lse, a.grad, a.grad_lse, a.grad_ent,          \
+                     a.entropy, reinterpret_cast<OUT_T*>(a.dlogits), a.ld_d, a.status)
   if (a.out_bf16) {
-    hipLaunchKernelGGL(bwd_dlogits<uint16_t>, grid, dim3(kBwdThreads), 0, stream, x, a.ld / 8,
-                       a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets, a.mask,
-                       a.ignore_index, a.lse, a.grad, reinterpret_cast<uint16_t*>(a.dlogits),
-                       a.ld_d, a.status);
+    if (ex) RLK_LAUNCH_BWD(uint16_t, true);
+    else RLK_LAUNCH_BWD(uint16_t, false);
   } else {
-    hipLaunchKernelGGL(bwd_dlogits<float>, grid, dim3(kBwdThreads), 0, stream, x, a.ld / 8,
-                       a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets, a.mask,
-                       a.ignore_index, a.lse, a.grad, reinterpret_cast<float*>(a.dlogits),
-                       a.ld_d, a.status);
+    if (ex) RLK_LAUNCH_BWD(float, true);
+    else RLK_LAUNCH_BWD(float, false);
   }
+#undef RLK_LAUNCH_BWD
   return hipGetLastError();
 }
 
