@@ -199,6 +199,9 @@ def main() -> int:
     ap.add_argument("--one-pass", action="store_true",
                     help="time rlk_logp_fwd_bwd (g known before the forward) instead of "
                          "rlk_logp_fwd + rlk_logp_bwd")
+    ap.add_argument("--extended", action="store_true",
+                    help="time rlk_logp_fwd_ex + rlk_logp_bwd_ex (entropy output; logp, LSE "
+                         "and entropy gradients) instead of rlk_logp_fwd + rlk_logp_bwd")
     ap.add_argument("--library-gemm", action="store_true",
                     help="LM-head workload: also time the library GEMM of the same shape")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -246,9 +249,19 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     one_pass = args.one_pass
-    if one_pass and not wl.backward:
-        log("bench: --one-pass needs a forward+backward workload")
+    extended = args.extended
+    if (one_pass or extended) and not wl.backward:
+        log("bench: --one-pass and --extended need a forward+backward workload")
         return 2
+    if one_pass and extended:
+        log("bench: --one-pass and --extended are separate schedules")
+        return 2
+    if extended:
+        ws = torch.empty(rlk.rlk_logp_ex_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        ent = torch.empty(n, dtype=torch.float32, device=dev)
+        gx = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+        g_lse = torch.randn(n, generator=gx, device=dev)
+        g_ent = torch.randn(n, generator=gx, device=dev)
 
     def step(i, events=None):
         b, m = inps[i % 2], masks[i % 2]
@@ -261,10 +274,16 @@ def main() -> int:
                 events[1].record(stream)
                 events[2].record(stream)
             return
-        rlk.rlk_logp_fwd(desc, b.logits, b.targets, m, logp, lse, ws, stream)
+        if extended:
+            rlk.rlk_logp_fwd_ex(desc, b.logits, b.targets, m, logp, lse, ent, ws, stream)
+        else:
+            rlk.rlk_logp_fwd(desc, b.logits, b.targets, m, logp, lse, ws, stream)
         if events:
             events[1].record(stream)
-        if wl.backward:
+        if extended:
+            rlk.rlk_logp_bwd_ex(desc, b.logits, b.targets, m, lse, ent, b.grad, g_lse, g_ent, dl,
+                                ld_d, code, ws, stream)
+        elif wl.backward:
             rlk.rlk_logp_bwd(desc, b.logits, b.targets, m, lse, b.grad, dl, ld_d, code, ws, stream)
         if events:
             events[2].record(stream)
@@ -304,6 +323,10 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic("fwd_bwd_rows"), "kernel": "fwd_bwd_rows"}
     else:
+        if extended:  # every row's logits are read again (the LSE and entropy terms reach all)
+            nb = dict(nb)
+            nb["fwd"] += 4 * n  # entropy out
+            nb["bwd"] += (n - (n_active + int(act1.sum())) // 2) * wl.real_vocab * 2 + 12 * n
         total_bytes = nb["fwd"] + (nb["bwd"] if wl.backward else 0)
         value = total_bytes / (ms_step * 1e-3) / 1e9
         fwd_gbs = nb["fwd"] / (fwd_ms * 1e-3) / 1e9
@@ -319,7 +342,8 @@ def main() -> int:
         dom_gbs = kernels[dom]["GB/s"]
         roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic("bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
+                    "traffic": None if extended else read_traffic(
+                        "bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
                     "kernel": dom}
 
     cpu = None
@@ -337,7 +361,8 @@ def main() -> int:
                    "vocab_tiles": wl.num_tiles, "virtual_shards": args.shards,
                    "dlogits_dtype": wl.dlogits_dtype, "parallelism": "single-gpu",
                    "schedule": "one launch (rlk_logp_fwd_bwd)" if one_pass
-                   else "rlk_logp_fwd then rlk_logp_bwd"},
+                   else ("rlk_logp_fwd_ex then rlk_logp_bwd_ex (entropy; logp, LSE and entropy "
+                         "gradients)" if extended else "rlk_logp_fwd then rlk_logp_bwd")},
         "tokens_per_s": round(n / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": total_bytes,

@@ -389,17 +389,44 @@ __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
                                                    const float* __restrict__ ps,
                                                    const float* __restrict__ pa,
                                                    int32_t num_tiles, float& H) {
-  float M = kNegInf;
-  for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
   H = __builtin_nanf("");
-  if (M == kNegInf) return kNegInf;
-  float S = 0.0f, A = 0.0f;
-  for (int32_t t = 0; t < num_tiles; ++t) {
-    const float mt = pm[t];
-    if (mt != kNegInf) {
-      const float e = expf(mt - M);
-      S = fmaf(ps[t], e, S);
-      A = fmaf(e, fmaf(mt - M, ps[t], pa[t]), A);
+  float M = kNegInf, S = 0.0f, A = 0.0f;
+  if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
+    // same arithmetic, with the loads issued up front as 16-byte vectors
+    float mv[kMergeVec], sv[kMergeVec], av[kMergeVec];
+#pragma unroll
+    for (int t = 0; t < kMergeVec; t += 4) {
+      if (t < num_tiles) {
+        const float4 a4 = *reinterpret_cast<const float4*>(pm + t);
+        const float4 b4 = *reinterpret_cast<const float4*>(ps + t);
+        const float4 c4 = *reinterpret_cast<const float4*>(pa + t);
+        mv[t] = a4.x; mv[t + 1] = a4.y; mv[t + 2] = a4.z; mv[t + 3] = a4.w;
+        sv[t] = b4.x; sv[t + 1] = b4.y; sv[t + 2] = b4.z; sv[t + 3] = b4.w;
+        av[t] = c4.x; av[t + 1] = c4.y; av[t + 2] = c4.z; av[t + 3] = c4.w;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMergeVec; ++t)
+      if (t < num_tiles) M = maxnan(M, mv[t]);
+    if (M == kNegInf) return kNegInf;
+#pragma unroll
+    for (int t = 0; t < kMergeVec; ++t) {
+      if (t < num_tiles && mv[t] != kNegInf) {
+        const float e = expf(mv[t] - M);
+        S = fmaf(sv[t], e, S);
+        A = fmaf(e, fmaf(mv[t] - M, sv[t], av[t]), A);
+      }
+    }
+  } else {
+    for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
+    if (M == kNegInf) return kNegInf;
+    for (int32_t t = 0; t < num_tiles; ++t) {
+      const float mt = pm[t];
+      if (mt != kNegInf) {
+        const float e = expf(mt - M);
+        S = fmaf(ps[t], e, S);
+        A = fmaf(e, fmaf(mt - M, ps[t], pa[t]), A);
+      }
     }
   }
   const float lS = logf(S);
@@ -535,12 +562,13 @@ __device__ __forceinline__ void dlogits_chunk(const uint4& q, int32_t j0, bool a
 // The extended gradient of the 8 columns [j0, j0 + 8) of one row, with the
 // LSE and entropy terms (the derivatives of LSE and of H = -sum p log p):
 //   d_j = g ([j == t] - p_j) + gl p_j - gh p_j (log p_j + H),  log p_j = x_j - L
-// computed as p_j (w - g) off the target and g (1 - p_t) + p_t w at it, with
-// w = gl - gh (x_j - L + H) (w = gl when gh == 0).  A column at -inf has
-// p = 0 and contributes 0 to every term (0 log 0 = 0).  `need` is false on a
-// row that no term reaches (it stays +0 and is not read); `bad` marks an
-// effective-active row with a target outside [0, V_real) (NaN on its real
-// columns).
+// computed off the target as fma(-gh, fma(p_j, H, p_j u_j), p_j c), c = gl - g,
+// and at the target as g (1 - p_t) + fma(-gh, fma(p_t, H, p_t u_t), p_t gl),
+// with u_j = max(x_j - L, -FLT_MAX): a column at -inf has p = 0 and adds 0 to
+// every term (0 log 0 = 0).  Without an entropy term (gh == 0, uniform over the
+// row) it is p_j c and g (1 - p_t) + p_t gl.  `need` is false on a row that no
+// term reaches (it stays +0 and is not read); `bad` marks an effective-active
+// row with a target outside [0, V_real) (NaN on its real columns).
 __device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, bool need, bool bad,
                                                  float L, float g, float gl, float gh, float H,
                                                  int32_t tgt, int32_t real_vocab,
@@ -557,14 +585,23 @@ __device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, boo
   } else {
     float x[8];
     unpack8(q, x);
-    float p[8], w[8];
+    const float c = gl - g;
+    float p[8], hv[8];
+    if (gh != 0.0f) {  // uniform over the row
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = x[e] - L;
-      p[e] = exp2_hw(t * kLog2e);
-      w[e] = gl;
-      if (gh != 0.0f) w[e] = (p[e] == 0.0f) ? 0.0f : gl - gh * (t + H);
-      d[e] = (p[e] == 0.0f) ? 0.0f : p[e] * (w[e] - g);
+      for (int e = 0; e < 8; ++e) {
+        const float t = x[e] - L;
+        p[e] = exp2_hw(t * kLog2e);
+        hv[e] = fmaf(p[e], H, p[e] * __builtin_fmaxf(t, -__FLT_MAX__));
+        d[e] = fmaf(-gh, hv[e], p[e] * c);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_hw((x[e] - L) * kLog2e);
+        hv[e] = 0.0f;
+        d[e] = p[e] * c;
+      }
     }
     if (j0 + 8 > real_vocab) {
 #pragma unroll
@@ -573,7 +610,7 @@ __device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, boo
     }
     if (tgt >= j0 && tgt < j0 + 8) {
       const int e = tgt - j0;
-      d[e] = g * (1.0f - p[e]) + p[e] * w[e];
+      d[e] = g * (1.0f - p[e]) + fmaf(-gh, hv[e], p[e] * gl);
     }
   }
 }
