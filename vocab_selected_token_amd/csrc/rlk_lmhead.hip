@@ -30,10 +30,14 @@
 // a token's reduction over the vocabulary stays mostly inside one lane.  The
 // 512 threads form 2 x 4 waves of 128 vocab x 64 tokens (4 x 2 MFMA tiles, 128
 // fp32 accumulators per lane), two waves per SIMD, so one wave's MFMAs run while
-// the other waits on memory.  K advances in slabs of 64 through double-buffered
-// LDS whose rows are padded from 128 to 144 bytes, so that the 16-byte fragment
-// reads of 8 consecutive lanes hit distinct banks; two register staging sets
-// keep the global loads of the next two slabs in flight.
+// the other waits on memory.  K advances in slabs of 64 through two LDS stages
+// filled by direct global-to-LDS loads (global_load_lds_dwordx4: lane i of an
+// instruction writes bytes [16i, 16i + 16) after the wave's LDS base), issued
+// for slab s+1 while slab s is multiplied.  LDS rows are 128 bytes with the
+// 16-byte chunks XOR-swizzled by row -- chunk c of row r sits at position
+// c ^ ((r >> 1) & 7) -- so that the fragment reads of 16 consecutive rows at
+// one chunk hit 16 distinct bank groups; each load lane fetches the chunk that
+// belongs at its position.
 //
 // Determinism: every reduction has a fixed order -- each lane over its rows in
 // register order, then the lane pair (l, l+32), then the two vocab halves of
@@ -57,21 +61,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kBV = 256;  // vocabulary rows per block (= kLmheadBlockVocab)
 constexpr int kBT = 256;  // tokens per block
 constexpr int kBK = 64;   // hidden-dimension slab per LDS stage
-constexpr int kRowBytes = kBK * 2 + 16;     // 144: padded LDS row
+constexpr int kRowBytes = kBK * 2;           // 128: one row of a slab, 8 chunks
 constexpr int kSlabBytes = kBV * kRowBytes;  // one operand, one stage
-constexpr int kRowsPerPass = kThreads / 8;   // 64 rows per thread pass (8 chunks per row)
-constexpr int kCopies = kBV / kRowsPerPass;  // 4 chunks per operand per thread per slab
+constexpr int kRowsPerLoad = 64 / (kRowBytes / 16);  // 8 rows per load instruction
+constexpr int kRowsPerWave = kBV / kWaves;           // 32 rows of each operand per wave
+constexpr int kLoads = kRowsPerWave / kRowsPerLoad;  // 4 instructions per operand per slab
 
 static_assert(kBV == kLmheadBlockVocab, "block width shared with the boundary");
-static_assert(kCopies == 4, "RLK_FOR4 spells out the four copies");
+static_assert(kBV == kBT, "the load mapping assumes square blocks");
 
-// Spell a 4-way loop out with literal indices, so the staging arrays are
-// promoted to registers before any loop unrolling happens.
-#define RLK_FOR4(M) M(0) M(1) M(2) M(3)
-static_assert(kBV == kBT, "the copy loop assumes square blocks");
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// LDS position (in 16-byte units) of chunk c of row r inside one operand stage.
+__device__ __forceinline__ int swizzled(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ float maxnan(float a, float b) {
   return __builtin_elementwise_maximum(a, b);
@@ -111,6 +117,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ seg_m,
     float* __restrict__ seg_s, float* __restrict__ tlogit) {
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kSlabBytes];
+  static_assert(2 * 2 * kSlabBytes >= kBT * 4 * (int)sizeof(float), "epilogue exchange fits");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,19 +143,19 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int32_t t0 = tb * kBT;
   const int32_t ldc = hidden_dim / 8;  // 16-byte chunks per row
 
-  // global -> LDS copy: thread tid moves chunk (tid & 7) of rows (tid >> 3) + 64j.
-  // Offsets are in 16-byte chunks from the operand base (the boundary checks
-  // that both operands hold fewer than 2^31 chunks).
-  const int kc = tid & 7;
-  const int r0 = tid >> 3;
-  int32_t woff[kCopies], hoff[kCopies];
-  // row clamps: padding rows of W and rows past the last token are never read
-#define RLK_OFFSETS(J)                                                                  \
-  woff[J] = min(v0 + r0 + kRowsPerPass * (J), real_vocab - 1) * ldc + kc;               \
-  hoff[J] = min(t0 + r0 + kRowsPerPass * (J), num_tokens - 1) * ldc + kc;
-  RLK_FOR4(RLK_OFFSETS)
-#undef RLK_OFFSETS
-  const int st_off = r0 * kRowBytes + kc * 16;
+  // Direct loads: wave w moves rows [32w, 32w + 32) of both operands, 8 rows per
+  // instruction; lane i of instruction j fetches row 32w + 8j + i/8 at the chunk
+  // that belongs at LDS position i%8.  Offsets are in 16-byte chunks from the
+  // operand base (the boundary checks that both operands hold fewer than 2^31
+  // chunks); padding rows of W and rows past the last token are never read.
+  int32_t woff[kLoads], hoff[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int row = wave * kRowsPerWave + j * kRowsPerLoad + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    woff[j] = min(v0 + row, real_vocab - 1) * ldc + c;
+    hoff[j] = min(t0 + row, num_tokens - 1) * ldc + c;
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -158,77 +165,51 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  // Two register staging sets give the global loads two slabs of MFMA work
-  // to arrive in: while slab s is multiplied out of LDS, slab s+1 waits in
-  // registers and slab s+2 is being fetched.
-  u32x4 sa0[kCopies], sb0[kCopies], sa1[kCopies], sb1[kCopies];
   const int nslab = hidden_dim / kBK;
-  const int32_t last = (nslab - 1) * (kBK / 8);
-  const int32_t second = min(kBK / 8, last);
-#define RLK_PROLOGUE_LOAD(J)        \
-  sa0[J] = w[woff[J]];              \
-  sb0[J] = h[hoff[J]];              \
-  sa1[J] = w[woff[J] + second];     \
-  sb1[J] = h[hoff[J] + second];
-  RLK_FOR4(RLK_PROLOGUE_LOAD)
-#undef RLK_PROLOGUE_LOAD
-#define RLK_PROLOGUE_STORE(J)                                                              \
-  *reinterpret_cast<u32x4*>(smem + st_off + (J) * kRowsPerPass * kRowBytes) = sa0[J];      \
-  *reinterpret_cast<u32x4*>(smem + kSlabBytes + st_off + (J) * kRowsPerPass * kRowBytes) = \
-      sb0[J];
-  RLK_FOR4(RLK_PROLOGUE_STORE)
-#undef RLK_PROLOGUE_STORE
+  // slab S into stage S & 1 (A = W rows at the stage base, B = hidden rows after)
+  auto issue = [&](int slab) __attribute__((always_inline)) {
+    char* base = smem + (slab & 1) * 2 * kSlabBytes + (wave * kRowsPerWave) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      __builtin_amdgcn_global_load_lds(w + woff[j] + slab * (kBK / 8),
+                                       (lds_ptr)(base + j * kRowsPerLoad * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(h + hoff[j] + slab * (kBK / 8),
+                                       (lds_ptr)(base + kSlabBytes + j * kRowsPerLoad * kRowBytes),
+                                       16, 0, 0);
+    }
+  };
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // fragment read offsets (bytes) inside one operand stage
+  // fragment reads: lane l takes row l%32 of each 32-row tile at chunk
+  // 2kk + l/32 (k in [16kk + 8(l/32), +8))
   const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 16;
-
-// One slab: fetch slab S+2 into LD_A/LD_B, multiply slab S out of LDS stage
-// S&1, then store slab S+1 from ST_A/ST_B into the other stage.  Slab indices
-// past the end are clamped to the last slab; those loads and stores are never
-// consumed.  (A macro rather than a lambda keeps every array in registers.)
-#define RLK_LMHEAD_SLAB_STEP(S, LD_A, LD_B, ST_A, ST_B)                                       \
-  do {                                                                                      \
-    const int32_t nxt_ = min(((S) + 2) * (kBK / 8), last);                                  \
-    LD_A[0] = w[woff[0] + nxt_]; LD_B[0] = h[hoff[0] + nxt_];                               \
-    LD_A[1] = w[woff[1] + nxt_]; LD_B[1] = h[hoff[1] + nxt_];                               \
-    LD_A[2] = w[woff[2] + nxt_]; LD_B[2] = h[hoff[2] + nxt_];                               \
-    LD_A[3] = w[woff[3] + nxt_]; LD_B[3] = h[hoff[3] + nxt_];                               \
-    const char* As_ = smem + ((S) & 1) * 2 * kSlabBytes;                                    \
-    const char* Bs_ = As_ + kSlabBytes;                                                     \
-    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                               \
-      bf16x8 af[4], bfr[2];                                                                 \
-      _Pragma("unroll") for (int vs = 0; vs < 4; ++vs) af[vs] =                             \
-          *reinterpret_cast<const bf16x8*>(                                                 \
-              As_ + (wv * 128 + vs * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);        \
-      _Pragma("unroll") for (int ts = 0; ts < 2; ++ts) bfr[ts] =                            \
-          *reinterpret_cast<const bf16x8*>(                                                 \
-              Bs_ + (wt * 64 + ts * 32 + frag_row) * kRowBytes + kk * 32 + frag_k);        \
-      _Pragma("unroll") for (int vs = 0; vs < 4; ++vs)                                      \
-          _Pragma("unroll") for (int ts = 0; ts < 2; ++ts) acc[vs][ts] =                    \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts], 0, 0, 0); \
-    }                                                                                       \
-    char* Ad_ = smem + (((S) + 1) & 1) * 2 * kSlabBytes + st_off;                           \
-    constexpr int kStep_ = kRowsPerPass * kRowBytes;                                        \
-    *reinterpret_cast<u32x4*>(Ad_ + 0 * kStep_) = ST_A[0];                                  \
-    *reinterpret_cast<u32x4*>(Ad_ + 1 * kStep_) = ST_A[1];                                  \
-    *reinterpret_cast<u32x4*>(Ad_ + 2 * kStep_) = ST_A[2];                                  \
-    *reinterpret_cast<u32x4*>(Ad_ + 3 * kStep_) = ST_A[3];                                  \
-    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 0 * kStep_) = ST_B[0];                     \
-    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 1 * kStep_) = ST_B[1];                     \
-    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 2 * kStep_) = ST_B[2];                     \
-    *reinterpret_cast<u32x4*>(Ad_ + kSlabBytes + 3 * kStep_) = ST_B[3];                     \
-    __syncthreads();                                                                        \
-  } while (0)
-
-  int s = 0;
-  for (; s + 1 < nslab; s += 2) {
-    RLK_LMHEAD_SLAB_STEP(s, sa0, sb0, sa1, sb1);      // slab s+2 -> set 0, s+1 from set 1
-    RLK_LMHEAD_SLAB_STEP(s + 1, sa1, sb1, sa0, sb0);  // slab s+3 -> set 1, s+2 from set 0
+  const int frag_c = lane >> 5;
+  for (int s = 0; s < nslab; ++s) {
+    if (s + 1 < nslab) issue(s + 1);  // the other stage was released by the last barrier
+    const char* As = smem + (s & 1) * 2 * kSlabBytes;
+    const char* Bs = As + kSlabBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+        af[vs] = *reinterpret_cast<const bf16x8*>(
+            As + swizzled(wv * 128 + vs * 32 + frag_row, kk * 2 + frag_c) * 16);
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+        bfr[ts] = *reinterpret_cast<const bf16x8*>(
+            Bs + swizzled(wt * 64 + ts * 32 + frag_row, kk * 2 + frag_c) * 16);
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+          acc[vs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // slab s+1 has landed in LDS
+    __syncthreads();
   }
-  if (s < nslab) RLK_LMHEAD_SLAB_STEP(s, sa0, sb0, sa1, sb1);
-#undef RLK_LMHEAD_SLAB_STEP
 
   // ---- epilogue -------------------------------------------------------------
   const int32_t bnd = inner_tile_bound(v0, padded_vocab, num_tiles);
