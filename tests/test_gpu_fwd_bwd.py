@@ -212,3 +212,35 @@ def test_side_stream():
         out = fused(inp, torch.float32)
     s.synchronize()
     assert_same_bits(out, ref, "side stream")
+
+
+def test_nonfinite_logits_match_separate_calls(orc):
+    """NaN, +inf and -inf among the real logits: the one-launch outputs agree with
+    the separate calls (NaN where they are NaN, bits elsewhere) and with the oracle."""
+    wl = W.small_workload(24, 151936, 152576, mask_keep=None, ignore_frac=0.0, seed=31)
+    inp = W.make_inputs(wl, DEV)
+    inp.logits[0, 100] = float("nan")
+    inp.logits[1, 7] = float("inf")
+    inp.logits[2, :] = float("-inf")
+    inp.logits[3, :50000] = float("-inf")
+    inp.logits[4, 151935] = float("nan")
+    m = torch.ones(24, dtype=torch.bool, device=DEV)
+    m[0] = False  # an inactive NaN row: LSE NaN, logp +0, dX +0
+    for dt in (torch.float32, torch.bfloat16):
+        out = fused(inp, dt, mask=m)
+        ref = rlk.forward(inp.logits, inp.targets, m, real_vocab=wl.real_vocab,
+                          padded_vocab=wl.padded_vocab, num_vocab_tiles=wl.num_tiles)
+        ref = ref + (rlk.backward(inp.logits, inp.targets, m, ref[1], inp.grad,
+                                  real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                                  out_dtype=dt, num_vocab_tiles=wl.num_tiles),)
+        for a, b, name in zip(out, ref, ("logp", "lse", "dlogits")):
+            na, nb = torch.isnan(a), torch.isnan(b)
+            assert torch.equal(na, nb), f"{dt} {name}: NaN pattern differs"
+            assert torch.equal(bits(a)[~na], bits(b)[~nb]), f"{dt} {name}: bits differ"
+        xb, tgt, mask, _ = W.to_host(inp)
+        mask = m.cpu().numpy()
+        lo, so, _, _ = orc.fwd(xb, tgt, mask, real_vocab=wl.real_vocab, raise_on_error=False)
+        lse = out[1].double().cpu().numpy()
+        assert np.array_equal(np.isnan(lse), np.isnan(so))
+        assert np.array_equal(np.isinf(lse), np.isinf(so))
+        assert (bits(out[2][0]) == 0).all() and bits(out[0][:1]).item() == 0
