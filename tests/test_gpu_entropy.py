@@ -267,3 +267,57 @@ def test_large_32k_entropy_sampled(orc):
                     g_ent=gh[sel].double().cpu().numpy())
     P.check_bwd_ex(P.dlogits_host(d[sel]), do, np.zeros(len(rows), dtype=bool), wl.real_vocab,
                    True, "32k", raw_bits(d[sel]))
+
+
+def test_extended_validate_and_bad_targets():
+    wl = W.small_workload(12, 5000, 5008, mask_keep=None, ignore_frac=0.0, seed=19)
+    inp = W.make_inputs(wl, DEV)
+    logp0, lse0, ent0 = fwd_ex(inp, validate=True)
+    g1, gl, gh = upstream(wl.num_tokens, 21)
+    d0 = bwd_ex(inp, lse0, ent0, g1, gl, gh, torch.float32)
+    inp.targets[4] = 5003  # a padded column: an error on an effective-active row
+    with pytest.raises(rlk.RlkError) as ei:
+        fwd_ex(inp, validate=True)
+    assert ei.value.status == rlk.RLK_ERR_TARGET_RANGE
+    logp, lse, ent = fwd_ex(inp)
+    keep = torch.arange(12, device=DEV) != 4
+    assert torch.isnan(logp[4]) and torch.equal(bits(lse), bits(lse0))
+    assert torch.equal(bits(ent), bits(ent0)) and torch.equal(bits(logp[keep]), bits(logp0[keep]))
+    with pytest.raises(rlk.RlkError) as ei:
+        rlk.backward_ex(inp.logits, inp.targets, inp.mask, lse, ent, g1, gl, gh,
+                        real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                        num_vocab_tiles=wl.num_tiles, validate=True)
+    assert ei.value.status == rlk.RLK_ERR_TARGET_RANGE
+    d = bwd_ex(inp, lse, ent, g1, gl, gh, torch.float32)
+    assert torch.isnan(d[4, :5000]).all() and (bits(d[4, 5000:]) == 0).all()
+    assert torch.equal(bits(d[keep]), bits(d0[keep]))
+    # an inactive row with a bad target is not an error: only its LSE/entropy terms remain
+    m = torch.ones(12, dtype=torch.bool, device=DEV)
+    m[4] = False
+    logp, lse, ent = rlk.forward_ex(inp.logits, inp.targets, m, real_vocab=wl.real_vocab,
+                                    padded_vocab=wl.padded_vocab, num_vocab_tiles=wl.num_tiles,
+                                    validate=True)
+    d = rlk.backward_ex(inp.logits, inp.targets, m, lse, ent, g1, gl, gh,
+                        real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                        num_vocab_tiles=wl.num_tiles, validate=True)
+    assert not torch.isnan(d[4]).any() and (d[4, :5000] != 0).any()
+
+
+def test_extended_side_stream():
+    wl = W.small_workload(40, 20000, 20000, seed=23)
+    inp = W.make_inputs(wl, DEV)
+    ref = fwd_ex(inp)
+    g1, gl, gh = upstream(wl.num_tokens, 22)
+    dref = bwd_ex(inp, ref[1], ref[2], g1, gl, gh, torch.bfloat16)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = rlk.forward_ex(inp.logits, inp.targets, inp.mask, real_vocab=wl.real_vocab,
+                             num_vocab_tiles=wl.num_tiles, stream=s)
+        d = rlk.backward_ex(inp.logits, inp.targets, inp.mask, out[1], out[2], g1, gl, gh,
+                            real_vocab=wl.real_vocab, out_dtype=torch.bfloat16,
+                            num_vocab_tiles=wl.num_tiles, stream=s)
+    s.synchronize()
+    for a, b in zip(out, ref):
+        assert torch.equal(bits(a), bits(b))
+    assert torch.equal(bits(d), bits(dref))
