@@ -327,3 +327,23 @@ def test_side_stream():
     s.synchronize()
     assert torch.equal(out[0].view(torch.int32), ref[0].view(torch.int32))
     assert torch.equal(out[1].view(torch.int32), ref[1].view(torch.int32))
+
+
+def test_small_and_large_launch_shapes_agree():
+    """Stage 1 packs a small batch into one-wave blocks and a large one into
+    four-wave blocks; a row gives the same bits either way (batch invariance
+    across the two launch shapes)."""
+    wl = W.small_workload(512, 151936, 152576, seed=27)  # 512 x 64 items: four-wave blocks
+    inp = W.make_inputs(wl, DEV)
+    big = fwd(inp)
+    for r0, r1 in ((0, 1), (5, 37), (100, 164), (448, 512)):  # small launches: one-wave blocks
+        sub = W.Inputs(wl, inp.logits[r0:r1], inp.targets[r0:r1], inp.mask[r0:r1],
+                       inp.grad[r0:r1])
+        part = fwd(sub)
+        assert torch.equal(part[0].view(torch.int32), big[0][r0:r1].view(torch.int32))
+        assert torch.equal(part[1].view(torch.int32), big[1][r0:r1].view(torch.int32))
+    # and the same for the entropy statistic
+    _, _, e_big = rlk.forward_ex(inp.logits, inp.targets, inp.mask, real_vocab=wl.real_vocab)
+    _, _, e_one = rlk.forward_ex(inp.logits[7:8], inp.targets[7:8], inp.mask[7:8],
+                                 real_vocab=wl.real_vocab)
+    assert torch.equal(e_one.view(torch.int32), e_big[7:8].view(torch.int32))

@@ -293,11 +293,13 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
 //   pent        [N][T] fp32, the entropy statistic (kEnt only)
 // Work item i = row * tile_count + (tile - tile_begin); group q of wave w of
 // work block b (the XCD-local renumbering of blockIdx.x) takes item
-// 16b + 4w + q.  Columns >= V_real never enter the arithmetic; chunks
-// that straddle a tile bound are masked by column index.
+// 4 (kWPB b + w) + q.  Columns >= V_real never enter the arithmetic; chunks
+// that straddle a tile bound are masked by column index.  kWPB (waves per
+// block) only decides how the waves are packed onto CUs -- one-wave blocks
+// spread a small batch over every CU -- so both launches give the same bits.
 // ---------------------------------------------------------------------------
-template <bool kEnt>
-__global__ __launch_bounds__(256) void stage1_partials(
+template <bool kEnt, int kWPB>
+__global__ __launch_bounds__(kWPB * 64) void stage1_partials(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t tile_begin,
     int32_t tile_count, float* __restrict__ pmax, float* __restrict__ psum,
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256) void stage1_partials(
   const int gl = lane & 15;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t block = xcd_local_block(blockIdx.x, gridDim.x);
-  const int64_t item0 = (block * kWavesPerBlock + wave_in_block) * kGroupsPerWave;
+  const int64_t item0 = (block * kWPB + wave_in_block) * kGroupsPerWave;
   const int64_t n_items = (int64_t)num_rows * tile_count;
 
   // item -> (row, tile) once per wave on the scalar unit, then step by grp
@@ -842,21 +844,30 @@ int64_t stage1_blocks(int64_t items) {
   return (items + per_block - 1) / per_block;
 }
 
+// Below this many 4-wave blocks a launch would leave CUs idle (two per CU on
+// the 256-CU part); smaller launches use one-wave blocks instead.
+constexpr int64_t kStage1SmallBlocks = 512;
+
 hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_rows * a.tile_count;
   if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)stage1_blocks(items));
+  const int64_t blocks4 = stage1_blocks(items);
+  const bool small = blocks4 < kStage1SmallBlocks;
+  const int wpb = small ? 1 : kWavesPerBlock;
+  const dim3 grid((unsigned)((items + wpb * kGroupsPerWave - 1) / (wpb * kGroupsPerWave)));
+  const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+#define RLK_LAUNCH_S1(ENT, WPB, PENT)                                                           \
+  hipLaunchKernelGGL((stage1_partials<ENT, WPB>), grid, dim3((WPB) * 64), 0, stream, x,       \
+                     a.ld / 8, a.num_rows, a.real_vocab, a.padded_vocab, a.num_tiles,         \
+                     a.tile_width, a.tile_begin, a.tile_count, a.pmax, a.psum, PENT)
   if (a.pent) {
-    hipLaunchKernelGGL(stage1_partials<true>, grid, dim3(kWavesPerBlock * 64), 0, stream,
-                       reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
-                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
-                       a.tile_count, a.pmax, a.psum, a.pent);
+    if (small) RLK_LAUNCH_S1(true, 1, a.pent);
+    else RLK_LAUNCH_S1(true, kWavesPerBlock, a.pent);
   } else {
-    hipLaunchKernelGGL(stage1_partials<false>, grid, dim3(kWavesPerBlock * 64), 0, stream,
-                       reinterpret_cast<const uint4*>(a.logits), a.ld / 8, a.num_rows,
-                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.tile_begin,
-                       a.tile_count, a.pmax, a.psum, nullptr);
+    if (small) RLK_LAUNCH_S1(false, 1, nullptr);
+    else RLK_LAUNCH_S1(false, kWavesPerBlock, nullptr);
   }
+#undef RLK_LAUNCH_S1
   return hipGetLastError();
 }
 
