@@ -45,13 +45,27 @@ def run(h, w, tgt, mask, v_real, v_pad, tiles, validate=False):
     return logp, lse, ws
 
 
+def draw_cases(count: int, seed: int):
+    """Seeded ragged shapes: tiles at least 256 columns wide, K a multiple of 64."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        v_real = int(rng.integers(256, 7000))
+        v_pad = v_real + int(rng.choice([0, 0, 5, 64, 300]))
+        tiles = int(rng.integers(1, v_pad // 256 + 1))
+        out.append(dict(n=int(rng.choice([1, 31, 255, 256, 257, 700])),
+                        k=int(rng.choice([64, 128, 256, 448])), v_real=v_real, v_pad=v_pad,
+                        tiles=tiles))
+    return out
+
+
 CASES = [
     dict(n=37, k=64, v_real=1000, v_pad=1024, tiles=4),
     dict(n=300, k=128, v_real=2500, v_pad=2560, tiles=10),
     dict(n=257, k=320, v_real=3000, v_pad=3000, tiles=7),
     dict(n=1, k=64, v_real=256, v_pad=256, tiles=1),
     dict(n=513, k=192, v_real=5000, v_pad=5120, tiles=3),
-]
+] + draw_cases(10, seed=4242)
 
 
 @pytest.mark.parametrize("c", CASES, ids=lambda c: "n{n}_k{k}_v{v_real}_p{v_pad}_T{tiles}".format(**c))
