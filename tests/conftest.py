@@ -19,3 +19,14 @@ def pytest_configure(config):
         build_lib = importlib.util.module_from_spec(spec)
         spec.loader.exec_module(build_lib)
         build_lib.build()
+    consumer = ROOT / "tests" / "_bin" / "abi_consumer"
+    if not consumer.exists():
+        import subprocess
+
+        import __graft_entry__
+
+        try:
+            __graft_entry__.build_abi_consumer()
+        except (OSError, subprocess.CalledProcessError) as exc:
+            # only the GPU test of the C consumer needs it; that test reports the absence
+            print(f"conftest: C ABI consumer not built: {exc}", file=sys.stderr)
