@@ -24,25 +24,32 @@
 //
 // GEMM layout.  The accumulator is C[vocab][token] = W . h^T: W rows are the
 // MFMA "A" operand and hidden rows the "B" operand, both K-contiguous.  With
-// v_mfma_f32_32x32x16_bf16, lane l supplies row/col l%32 and k in
-// [8*(l/32), 8*(l/32)+8); accumulator i of lane l is C[8*(i/4) + 4*(l/32) +
-// i%4][l%32].  So each lane holds 16 vocab rows of one token per 32x32 tile and
-// a token's reduction over the vocabulary stays mostly inside one lane.  The
-// 512 threads form 2 x 4 waves of 128 vocab x 64 tokens (4 x 2 MFMA tiles, 128
-// fp32 accumulators per lane), two waves per SIMD, so one wave's MFMAs run while
-// the other waits on memory.  K advances in slabs of 64 through two LDS stages
-// filled by direct global-to-LDS loads (global_load_lds_dwordx4: lane i of an
-// instruction writes bytes [16i, 16i + 16) after the wave's LDS base), issued
-// for slab s+1 while slab s is multiplied.  LDS rows are 128 bytes with the
-// 16-byte chunks XOR-swizzled by row -- chunk c of row r sits at position
-// c ^ ((r >> 1) & 7) -- so that the fragment reads of 16 consecutive rows at
-// one chunk hit 16 distinct bank groups; each load lane fetches the chunk that
-// belongs at its position.
+// v_mfma_f32_16x16x32_bf16, lane l supplies row/col l%16 and k in
+// [8*(l/16), 8*(l/16)+8) of a 32-wide k-step; accumulator i of lane l is
+// C[4*(l/16) + i][l%16].  So each lane holds 4 vocab rows of one token per
+// 16x16 tile, and a wave's rows of one token sit in the four lanes
+// l%16 + 16g.  The 512 threads form 2 x 4 waves of 128 vocab x 64 tokens
+// (8 x 4 MFMA tiles, 128 fp32 accumulators per lane), two waves per SIMD, so
+// one wave's MFMAs run while the other waits on memory.
+//
+// K advances in slabs of 64 (two k-steps) through two LDS stages filled by
+// direct global-to-LDS loads (global_load_lds_dwordx4: lane i of an
+// instruction writes bytes [16i, 16i + 16) after the wave's LDS base).  LDS
+// rows are 128 bytes with the 16-byte chunks XOR-swizzled by row -- chunk c of
+// row r sits at position c ^ ((r >> 1) & 7) -- so that fragment reads of
+// consecutive rows at one chunk spread over the bank groups; each load lane
+// fetches the chunk that belongs at its position.  One barrier per slab, placed
+// before the slab's last k-step: by then every wave has read the slab's
+// fragments into registers, so the DMA for slab s+2 can go into the stage just
+// released, and the first fragments of slab s+1 are read while the last k-step's
+// MFMAs run.  Inside each k-step the next fragment reads (and the slab loads)
+// are spread between the MFMAs.
 //
 // Determinism: every reduction has a fixed order -- each lane over its rows in
-// register order, then the lane pair (l, l+32), then the two vocab halves of
-// the block (the lower half first), then the segments of a tile in ascending
-// column order, then the tiles in stage 2.  No atomics.
+// register order, then the four lanes of a token by xor-shuffles over 16 and
+// 32 lanes (commutative additions, so all four lanes hold the same bits), then
+// the two vocab halves of the block (the lower half first), then the segments
+// of a tile in ascending column order, then the tiles in stage 2.  No atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,7 +59,7 @@ namespace rlk {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16 bytes as a native vector: arrays of it stay in registers (HIP's uint4 is
 // a struct around a union, which keeps arrays of it in scratch memory)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -157,18 +164,20 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     hoff[j] = min(t0 + row, num_tokens - 1) * ldc + c;
   }
 
-  f32x16 acc[4][2];
+  constexpr int kVS = 8;  // 16-row vocabulary tiles per wave
+  constexpr int kTS = 4;  // 16-token tiles per wave
+  f32x4 acc[kVS][kTS];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kVS; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kTS; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+      for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
 
   const int nslab = hidden_dim / kBK;
-  // slab S into stage S & 1 (A = W rows at the stage base, B = hidden rows after)
-  auto issue = [&](int slab) __attribute__((always_inline)) {
-    char* base = smem + (slab & 1) * 2 * kSlabBytes + (wave * kRowsPerWave) * kRowBytes;
+  // slab `slab` into LDS stage `stage` (A = W rows at the stage base, B = hidden rows after)
+  auto issue = [&](int slab, int stage) __attribute__((always_inline)) {
+    char* base = smem + stage * 2 * kSlabBytes + (wave * kRowsPerWave) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       __builtin_amdgcn_global_load_lds(w + woff[j] + slab * (kBK / 8),
@@ -178,50 +187,94 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
                                        16, 0, 0);
     }
   };
-  issue(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // fragment reads: lane l takes row l%32 of each 32-row tile at chunk
-  // 2kk + l/32 (k in [16kk + 8(l/32), +8))
-  const int frag_row = lane & 31;
-  const int frag_c = lane >> 5;
-  for (int s = 0; s < nslab; ++s) {
-    if (s + 1 < nslab) issue(s + 1);  // the other stage was released by the last barrier
-    const char* As = smem + (s & 1) * 2 * kSlabBytes;
+  // fragment reads of k-step ks: lane l takes row l%16 of each 16-row tile at
+  // chunk 4ks + l/16 (k in [32ks + 8(l/16), +8))
+  const int frag_row = lane & 15;
+  const int frag_c = lane >> 4;
+  auto fetch = [&](const char* As, int ks, bf16x8 (&af)[kVS], bf16x8 (&bf)[kTS])
+      __attribute__((always_inline)) {
     const char* Bs = As + kSlabBytes;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[4], bfr[2];
+    for (int vs = 0; vs < kVS; ++vs)
+      af[vs] = *reinterpret_cast<const bf16x8*>(
+          As + swizzled(wv * 128 + vs * 16 + frag_row, ks * 4 + frag_c) * 16);
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
-        af[vs] = *reinterpret_cast<const bf16x8*>(
-            As + swizzled(wv * 128 + vs * 32 + frag_row, kk * 2 + frag_c) * 16);
+    for (int ts = 0; ts < kTS; ++ts)
+      bf[ts] = *reinterpret_cast<const bf16x8*>(
+          Bs + swizzled(wt * 64 + ts * 16 + frag_row, ks * 4 + frag_c) * 16);
+  };
+  auto mma = [&](const bf16x8 (&af)[kVS], const bf16x8 (&bf)[kTS]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts)
-        bfr[ts] = *reinterpret_cast<const bf16x8*>(
-            Bs + swizzled(wt * 64 + ts * 32 + frag_row, kk * 2 + frag_c) * 16);
+    for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int ts = 0; ts < kTS; ++ts)
+        acc[vs][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[vs], bf[ts], acc[vs][ts], 0, 0, 0);
+  };
+  // Instruction order inside a k-step: 4 MFMAs, then one fragment read (and,
+  // after the barrier, one slab load) per 2 MFMAs, then the remaining MFMAs.
+  // The reads thus overlap the MFMAs that do not need them.
+  constexpr int kReads = kVS + kTS, kMfmas = kVS * kTS, kLead = 4, kPer = 2;
+  static_assert(kLead + kPer * kReads <= kMfmas, "the reads fit inside the step");
+  static_assert(2 * kLoads <= kReads, "one load per read at most");
+  auto order_step = [&](bool with_loads) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);  // MFMA
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
-          acc[vs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vs], bfr[ts], acc[vs][ts], 0, 0, 0);
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (with_loads && i < 2 * kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // slab s+1 has landed in LDS
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kLead - kPer * kReads, 0);
+  };
+  // s_waitcnt immediate with lgkmcnt = 0 and the other counters at their maxima
+  constexpr int kWaitLds = 0xC07F;
+
+  issue(0, 0);
+  if (nslab > 1) issue(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  bf16x8 a0[kVS], b0[kTS], a1[kVS], b1[kTS];
+  fetch(smem, 0, a0, b0);
+  for (int s = 0; s < nslab; ++s) {
+    const char* cur = smem + (s & 1) * 2 * kSlabBytes;
+    const char* nxt = smem + ((s + 1) & 1) * 2 * kSlabBytes;
+    // the fragments of this k-step were read during the previous one; wait for
+    // them before more reads go out (the LDS counter holds at most 15)
+    __builtin_amdgcn_s_waitcnt(kWaitLds);
+    fetch(cur, 1, a1, b1);
+    mma(a0, b0);
+    order_step(false);
+    __builtin_amdgcn_sched_barrier(0);
+    // every wave has read slab s into registers, and slab s+1 (issued one
+    // slab ago) has landed in the other stage
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // slab s+2 into the stage just released.  The last two steps reload slab
+    // nslab-1 there and read the other stage's first fragments, which nothing
+    // uses: the loads and reads stay unconditional, so they can be interleaved
+    // with the MFMAs, and stay in bounds.
+    issue(min(s + 2, nslab - 1), s & 1);
+    fetch(nxt, 0, a0, b0);
+    mma(a1, b1);
+    order_step(true);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // the reloads of the last two steps land before the epilogue reuses the stages
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // ---- epilogue -------------------------------------------------------------
   const int32_t bnd = inner_tile_bound(v0, padded_vocab, num_tiles);
   const int32_t vw0 = v0 + wv * 128;            // first vocabulary row of this wave
-  const int32_t row_lane = 4 * (lane >> 5);     // lane-half offset inside an 8-row group
+  const int32_t row_lane = 4 * (lane >> 4);     // lane-group offset inside a 16-row tile
   float* xch = reinterpret_cast<float*>(smem);  // [256 tokens][4]
   // every row of the block is real and no tile bound cuts it: one segment, no masks
   const bool simple = (v0 + kBV <= real_vocab) && (bnd == v0 + kBV);
 
 #pragma unroll
-  for (int ts = 0; ts < 2; ++ts) {
-    const int32_t tok = t0 + wt * 64 + ts * 32 + (lane & 31);
+  for (int ts = 0; ts < kTS; ++ts) {
+    const int32_t tok = t0 + wt * 64 + ts * 16 + (lane & 15);
     int32_t trow = -1;  // the target's column if this wave holds it
     if (tok < num_tokens && (mask == nullptr || mask[tok] != 0)) {
       const int32_t tg = targets[tok];
@@ -231,10 +284,10 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
       float tz = 0.0f;
       bool have_t = false;
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+        for (int i = 0; i < 4; ++i) {
+          const int32_t row = vw0 + vs * 16 + row_lane + i;
           if (row == trow) {
             tz = acc[vs][ts][i];
             have_t = true;
@@ -245,30 +298,33 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     float m0 = kNegInf, m1 = kNegInf, s0 = 0.0f, s1 = 0.0f;
     if (simple) {
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m0 = maxnan(m0, acc[vs][ts][i]);
-      // the lane pair (l, l+32) holds the other rows of the same token
+        for (int i = 0; i < 4; ++i) m0 = maxnan(m0, acc[vs][ts][i]);
+      // the lanes l%16 + 16g hold the other rows of the same token
+      m0 = maxnan(m0, __shfl_xor(m0, 16));
       m0 = maxnan(m0, __shfl_xor(m0, 32));
       const float b0 = (m0 == kNegInf) ? 0.0f : m0;
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
+        for (int i = 0; i < 4; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
     } else {
       // pass 1: per-segment maxima over this lane's real rows
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+        for (int i = 0; i < 4; ++i) {
+          const int32_t row = vw0 + vs * 16 + row_lane + i;
           const float z = acc[vs][ts][i];
           if (row < real_vocab && row < bnd) m0 = maxnan(m0, z);
           if (row < real_vocab && row >= bnd) m1 = maxnan(m1, z);
         }
+      m0 = maxnan(m0, __shfl_xor(m0, 16));
       m0 = maxnan(m0, __shfl_xor(m0, 32));
+      m1 = maxnan(m1, __shfl_xor(m1, 16));
       m1 = maxnan(m1, __shfl_xor(m1, 32));
-      // pass 2: sums of exp(z - max) relative to the pair maxima.  The two
+      // pass 2: sums of exp(z - max) relative to the token's maxima.  The two
       // thresholds go through an empty asm so the compiler recomputes the row
       // tests here instead of keeping 128 masks alive from pass 1.
       int32_t rv = real_vocab, bd = bnd;
@@ -276,10 +332,10 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
       const float b0 = (m0 == kNegInf) ? 0.0f : m0;
       const float b1 = (m1 == kNegInf) ? 0.0f : m1;
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t row = vw0 + vs * 32 + 8 * (i >> 2) + row_lane + (i & 3);
+        for (int i = 0; i < 4; ++i) {
+          const int32_t row = vw0 + vs * 16 + row_lane + i;
           const float z = (row < rv) ? acc[vs][ts][i] : kNegInf;
           const bool hi = row >= bd;
           const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
@@ -287,12 +343,14 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
           s1 += hi ? e : 0.0f;
         }
     }
-    // lane pair: the same two addends in both lanes, so both hold the same sum
-    const float p0 = __shfl_xor(s0, 32), p1 = __shfl_xor(s1, 32);
-    s0 = (lane < 32) ? s0 + p0 : p0 + s0;
-    s1 = (lane < 32) ? s1 + p1 : p1 + s1;
-    if (wv == 1 && lane < 32) {
-      float* x = xch + ((wt * 64 + ts * 32 + lane) * 4);
+    // the four lanes of the token: pairs over 16 lanes, then over 32; each
+    // addition has the same two addends in both lanes, so all four agree
+    s0 += __shfl_xor(s0, 16);
+    s1 += __shfl_xor(s1, 16);
+    s0 += __shfl_xor(s0, 32);
+    s1 += __shfl_xor(s1, 32);
+    if (wv == 1 && lane < 16) {
+      float* x = xch + ((wt * 64 + ts * 16 + lane) * 4);
       x[0] = m0;
       x[1] = s0;
       x[2] = m1;
@@ -307,13 +365,13 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     }
   }
   __syncthreads();
-  if (wv == 0 && lane < 32) {
+  if (wv == 0 && lane < 16) {
     const int64_t seg_ld = 2 * (int64_t)n_vb;
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts) {
-      const int32_t tok = t0 + wt * 64 + ts * 32 + lane;
+    for (int ts = 0; ts < kTS; ++ts) {
+      const int32_t tok = t0 + wt * 64 + ts * 16 + lane;
       if (tok >= num_tokens) continue;
-      const float* x = xch + ((wt * 64 + ts * 32 + lane) * 4);
+      const float* x = xch + ((wt * 64 + ts * 16 + lane) * 4);
       float out_m[2], out_s[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
