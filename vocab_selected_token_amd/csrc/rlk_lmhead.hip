@@ -178,14 +178,16 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   // slab `slab` into LDS stage `stage` (A = W rows at the stage base, B = hidden rows after)
   auto issue = [&](int slab, int stage) __attribute__((always_inline)) {
     char* base = smem + stage * 2 * kSlabBytes + (wave * kRowsPerWave) * kRowBytes;
+    // all W rows, then all hidden rows (about 0.6% faster than alternating)
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kLoads; ++j)
       __builtin_amdgcn_global_load_lds(w + woff[j] + slab * (kBK / 8),
                                        (lds_ptr)(base + j * kRowsPerLoad * kRowBytes), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
       __builtin_amdgcn_global_load_lds(h + hoff[j] + slab * (kBK / 8),
                                        (lds_ptr)(base + kSlabBytes + j * kRowsPerLoad * kRowBytes),
                                        16, 0, 0);
-    }
   };
   // fragment reads of k-step ks: lane l takes row l%16 of each 16-row tile at
   // chunk 4ks + l/16 (k in [32ks + 8(l/16), +8))
