@@ -140,6 +140,25 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
   v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
 }
 
+// NC consecutive bf16 logits of one row as loaded: 8 from a 16-byte load, or
+// 4 from an 8-byte load
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int NC>
+struct Cols;
+template <>
+struct Cols<8> {
+  typedef uint4 T;
+  static __device__ __forceinline__ void unpack(const uint4& q, float* v) { unpack8(q, v); }
+};
+template <>
+struct Cols<4> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ void unpack(const u32x2& q, float* v) {
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  }
+};
+
 // A pass: slot k (k < kChunks) of lane gl of the group is chunk b + 16k + gl.
 // Slots outside the tile's full chunks [lo_c, hi_c) are loaded from a clamped
 // address (nothing outside the tile is read) and hold -inf, which adds
@@ -487,7 +506,11 @@ struct Store8;
 
 template <>
 struct Store8<float> {
-  // out points at the chunk's first column; n = columns to write (1..8)
+  // out points at the chunk's first column; n = columns to write (1..8).  Used
+  // by the one-launch kernel only (the separate backward writes fp32 in
+  // 4-column pieces).  Nontemporal: plain stores, although L2 would merge a
+  // lane's two 16-byte halves with its neighbours', displace the lines that
+  // kernel reads a second time (1024 rows: 0.269 ms against 0.244).
   static __device__ __forceinline__ void store(float* out, const float* d, int n) {
     if (n == 8) {
       uint4* o = reinterpret_cast<uint4*>(out);
@@ -523,7 +546,7 @@ struct Store8<uint16_t> {
   }
 };
 
-// dX of the 8 columns [j0, j0 + 8) of one row (q = their logits, read only on
+// dX of the NC columns [j0, j0 + NC) of one row (q = their logits, read only on
 // an effective-active row with a good target and j0 < V_real):
 //   inactive row                 +0
 //   bad target                   NaN on real columns, +0 on padded ones
@@ -531,37 +554,38 @@ struct Store8<uint16_t> {
 //                                at the target t
 //   padded column                +0
 // exp(y) is taken as exp2(y * log2 e) on the hardware unit, in one fixed form.
-__device__ __forceinline__ void dlogits_chunk(const uint4& q, int32_t j0, bool act, bool bad,
-                                              float L, float g, int32_t tgt, int32_t real_vocab,
-                                              float (&d)[8]) {
+template <int NC>
+__device__ __forceinline__ void dlogits_chunk(const typename Cols<NC>::T& q, int32_t j0, bool act,
+                                              bool bad, float L, float g, int32_t tgt,
+                                              int32_t real_vocab, float (&d)[NC]) {
   if (!act) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = 0.0f;
   } else if (bad) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
   } else if (j0 >= real_vocab) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = 0.0f;
   } else {
-    float x[8];
-    unpack8(q, x);
+    float x[NC];
+    Cols<NC>::unpack(q, x);
     const float ng = -g;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
-    if (j0 + 8 > real_vocab) {
+    for (int e = 0; e < NC; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
+    if (j0 + NC > real_vocab) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < NC; ++e)
         if (j0 + e >= real_vocab) d[e] = 0.0f;
     }
-    if (tgt >= j0 && tgt < j0 + 8) {
+    if (tgt >= j0 && tgt < j0 + NC) {
       const int e = tgt - j0;
       d[e] = g * (1.0f - exp2_hw((x[e] - L) * kLog2e));
     }
   }
 }
 
-// The extended gradient of the 8 columns [j0, j0 + 8) of one row, with the
+// The extended gradient of the NC columns [j0, j0 + NC) of one row, with the
 // LSE and entropy terms (the derivatives of LSE and of H = -sum p log p):
 //   d_j = g ([j == t] - p_j) + gl p_j - gh p_j (log p_j + H),  log p_j = x_j - L
 // computed off the target as fma(-gh, fma(p_j, H, p_j u_j), p_j c), c = gl - g,
@@ -571,27 +595,28 @@ __device__ __forceinline__ void dlogits_chunk(const uint4& q, int32_t j0, bool a
 // row) it is p_j c and g (1 - p_t) + p_t gl.  `need` is false on a row that no
 // term reaches (it stays +0 and is not read); `bad` marks an effective-active
 // row with a target outside [0, V_real) (NaN on its real columns).
-__device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, bool need, bool bad,
-                                                 float L, float g, float gl, float gh, float H,
-                                                 int32_t tgt, int32_t real_vocab,
-                                                 float (&d)[8]) {
+template <int NC>
+__device__ __forceinline__ void dlogits_chunk_ex(const typename Cols<NC>::T& q, int32_t j0,
+                                                 bool need, bool bad, float L, float g, float gl,
+                                                 float gh, float H, int32_t tgt,
+                                                 int32_t real_vocab, float (&d)[NC]) {
   if (!need) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = 0.0f;
   } else if (bad) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = (j0 + e < real_vocab) ? __builtin_nanf("") : 0.0f;
   } else if (j0 >= real_vocab) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int e = 0; e < NC; ++e) d[e] = 0.0f;
   } else {
-    float x[8];
-    unpack8(q, x);
+    float x[NC];
+    Cols<NC>::unpack(q, x);
     const float c = gl - g;
-    float p[8], hv[8];
+    float p[NC], hv[NC];
     if (gh != 0.0f) {  // uniform over the row
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < NC; ++e) {
         const float t = x[e] - L;
         p[e] = exp2_hw(t * kLog2e);
         hv[e] = fmaf(p[e], H, p[e] * __builtin_fmaxf(t, -__FLT_MAX__));
@@ -599,18 +624,18 @@ __device__ __forceinline__ void dlogits_chunk_ex(const uint4& q, int32_t j0, boo
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < NC; ++e) {
         p[e] = exp2_hw((x[e] - L) * kLog2e);
         hv[e] = 0.0f;
         d[e] = p[e] * c;
       }
     }
-    if (j0 + 8 > real_vocab) {
+    if (j0 + NC > real_vocab) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < NC; ++e)
         if (j0 + e >= real_vocab) d[e] = 0.0f;
     }
-    if (tgt >= j0 && tgt < j0 + 8) {
+    if (tgt >= j0 && tgt < j0 + NC) {
       const int e = tgt - j0;
       d[e] = g * (1.0f - p[e]) + fmaf(-gh, hv[e], p[e] * gl);
     }
@@ -645,6 +670,44 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
   const float L = need ? lse[row] : 0.0f;
   const float g = (act && (!kEx || grad)) ? grad[row] : 0.0f;
   OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
+  if constexpr (sizeof(OutT) == 4) {
+    // fp32 dX in 4-column pieces from 8-byte loads: each lane's 16-byte store
+    // then lands next to its neighbours', and a wave's store instruction writes
+    // 1 KB contiguous.  (Two 16-byte stores per lane at a 32-byte lane stride,
+    // nontemporal, ran the read-write mix at about 4.0 TB/s against 5.8.)
+    constexpr int kPieces = kBwdCols / 4 / kBwdThreads;
+    const u32x2* __restrict__ xq =
+        reinterpret_cast<const u32x2*>(logits) + (int64_t)row * (ld_chunks * 2);
+    const int32_t p0 = cb * (kBwdCols / 4) + threadIdx.x;
+    u32x2 q[kPieces];
+    if (need && !bad) {
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        const int32_t pc = p0 + k * kBwdThreads;
+        if ((pc << 2) < real_vocab) q[k] = __builtin_nontemporal_load(xq + pc);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int32_t j0 = (p0 + k * kBwdThreads) << 2;
+      if (j0 >= padded_vocab) continue;
+      float d[4];
+      if (kEx)
+        dlogits_chunk_ex(q[k], j0, need, bad, L, g, gl, gh, H, act ? tgt : -1, real_vocab, d);
+      else
+        dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
+      float* o = reinterpret_cast<float*>(orow) + j0;
+      if (j0 + 4 <= padded_vocab) {
+        __builtin_nontemporal_store(
+            u32x4{__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
+                  __float_as_uint(d[3])},
+            reinterpret_cast<u32x4*>(o));
+      } else {
+        for (int e = 0; e < padded_vocab - j0; ++e) o[e] = d[e];
+      }
+    }
+    return;
+  }
   const uint4* __restrict__ xrow = logits + (int64_t)row * ld_chunks;
   const int32_t c0 = cb * (kBwdCols / 8) + threadIdx.x;
 
