@@ -501,28 +501,9 @@ constexpr int kBwdThreads = 128;
 constexpr int kBwdUnroll = 2;
 constexpr int kBwdCols = kBwdThreads * 8 * kBwdUnroll;  // 2048 columns
 
+// bf16 dX of 8 columns (the fp32 kernels write 4-column pieces, store_quad)
 template <typename OutT>
 struct Store8;
-
-template <>
-struct Store8<float> {
-  // out points at the chunk's first column; n = columns to write (1..8).  Used
-  // by the one-launch kernel only (the separate backward writes fp32 in
-  // 4-column pieces).  Nontemporal: plain stores, although L2 would merge a
-  // lane's two 16-byte halves with its neighbours', displace the lines that
-  // kernel reads a second time (1024 rows: 0.269 ms against 0.244).
-  static __device__ __forceinline__ void store(float* out, const float* d, int n) {
-    if (n == 8) {
-      uint4* o = reinterpret_cast<uint4*>(out);
-      store_stream(o, make_uint4(__float_as_uint(d[0]), __float_as_uint(d[1]),
-                                 __float_as_uint(d[2]), __float_as_uint(d[3])));
-      store_stream(o + 1, make_uint4(__float_as_uint(d[4]), __float_as_uint(d[5]),
-                                     __float_as_uint(d[6]), __float_as_uint(d[7])));
-    } else {
-      for (int e = 0; e < n; ++e) out[e] = d[e];
-    }
-  }
-};
 
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   // two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
@@ -545,6 +526,19 @@ struct Store8<uint16_t> {
     }
   }
 };
+
+// fp32 dX of 4 columns at out (16-byte aligned); n = columns to write (1..4).
+// In the 4-column layout a wave's stores cover 1 KB contiguous, so the
+// nontemporal hint costs nothing.
+__device__ __forceinline__ void store_quad(float* out, const float (&d)[4], int n) {
+  if (n == 4) {
+    __builtin_nontemporal_store(u32x4{__float_as_uint(d[0]), __float_as_uint(d[1]),
+                                      __float_as_uint(d[2]), __float_as_uint(d[3])},
+                                reinterpret_cast<u32x4*>(out));
+  } else {
+    for (int e = 0; e < n; ++e) out[e] = d[e];
+  }
+}
 
 // dX of the NC columns [j0, j0 + NC) of one row (q = their logits, read only on
 // an effective-active row with a good target and j0 < V_real):
@@ -696,40 +690,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
         dlogits_chunk_ex(q[k], j0, need, bad, L, g, gl, gh, H, act ? tgt : -1, real_vocab, d);
       else
         dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
-      float* o = reinterpret_cast<float*>(orow) + j0;
-      if (j0 + 4 <= padded_vocab) {
-        __builtin_nontemporal_store(
-            u32x4{__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
-                  __float_as_uint(d[3])},
-            reinterpret_cast<u32x4*>(o));
-      } else {
-        for (int e = 0; e < padded_vocab - j0; ++e) o[e] = d[e];
+      store_quad(reinterpret_cast<float*>(orow) + j0, d, min(4, padded_vocab - j0));
+    }
+  } else {
+    // bf16 dX: 2 chunks of 8 columns per thread, 16-byte loads and stores
+    const uint4* __restrict__ xrow = logits + (int64_t)row * ld_chunks;
+    const int32_t c0 = cb * (kBwdCols / 8) + threadIdx.x;
+    uint4 q[kBwdUnroll];
+    if (need && !bad) {
+#pragma unroll
+      for (int k = 0; k < kBwdUnroll; ++k) {
+        const int32_t c = c0 + k * kBwdThreads;
+        if ((c << 3) < real_vocab) q[k] = xrow[c];
       }
     }
-    return;
-  }
-  const uint4* __restrict__ xrow = logits + (int64_t)row * ld_chunks;
-  const int32_t c0 = cb * (kBwdCols / 8) + threadIdx.x;
-
-  uint4 q[kBwdUnroll];
-  if (need && !bad) {
 #pragma unroll
     for (int k = 0; k < kBwdUnroll; ++k) {
       const int32_t c = c0 + k * kBwdThreads;
-      if ((c << 3) < real_vocab) q[k] = xrow[c];
+      const int32_t j0 = c << 3;
+      if (j0 >= padded_vocab) continue;
+      float d[8];
+      if (kEx)
+        dlogits_chunk_ex(q[k], j0, need, bad, L, g, gl, gh, H, act ? tgt : -1, real_vocab, d);
+      else
+        dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
+      Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
     }
-  }
-#pragma unroll
-  for (int k = 0; k < kBwdUnroll; ++k) {
-    const int32_t c = c0 + k * kBwdThreads;
-    const int32_t j0 = c << 3;
-    if (j0 >= padded_vocab) continue;
-    float d[8];
-    if (kEx)
-      dlogits_chunk_ex(q[k], j0, need, bad, L, g, gl, gh, H, act ? tgt : -1, real_vocab, d);
-    else
-      dlogits_chunk(q[k], j0, act, bad, L, g, tgt, real_vocab, d);
-    Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
   }
 }
 
@@ -828,14 +814,28 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
       s_s[tile] = ls;
     }
   }
+  // the first batch of phase-3 loads: 16-byte chunks of 8 columns, or for fp32
+  // dX 8-byte pieces of 4 columns (see bwd_dlogits)
+  constexpr bool kQuad = sizeof(OutT) == 4;
+  constexpr int kPieces = 2 * kFbUnroll;
+  const u32x2* __restrict__ rowq = reinterpret_cast<const u32x2*>(rowp);
   const int32_t n_chunks = (padded_vocab + 7) >> 3;
   int32_t c0 = threadIdx.x;
   uint4 qa[kFbUnroll], qb[kFbUnroll];
+  u32x2 pa[kPieces], pb[kPieces];
   if (reread) {
+    if constexpr (kQuad) {
 #pragma unroll
-    for (int k = 0; k < kFbUnroll; ++k) {
-      const int32_t c = c0 + k * kFbThreads;
-      if ((c << 3) < real_vocab) qa[k] = load_stream(rowp + c);
+      for (int k = 0; k < kPieces; ++k) {
+        const int32_t pc = c0 + k * kFbThreads;
+        if ((pc << 2) < real_vocab) pa[k] = __builtin_nontemporal_load(rowq + pc);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFbUnroll; ++k) {
+        const int32_t c = c0 + k * kFbThreads;
+        if ((c << 3) < real_vocab) qa[k] = load_stream(rowp + c);
+      }
     }
   }
   __syncthreads();
@@ -870,26 +870,50 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
   //    are not read again)
   const float L = act ? s_lse : 0.0f;
   OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
-  for (; c0 < n_chunks; c0 += kFbThreads * kFbUnroll) {
-    const int32_t c1 = c0 + kFbThreads * kFbUnroll;
-    if (reread && c1 < n_chunks) {
+  if constexpr (kQuad) {
+    const int32_t n_quads = (padded_vocab + 3) >> 2;
+    for (int32_t p0 = threadIdx.x; p0 < n_quads; p0 += kFbThreads * kPieces) {
+      const int32_t p1 = p0 + kFbThreads * kPieces;
+      if (reread && p1 < n_quads) {
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) {
+          const int32_t pc = p1 + k * kFbThreads;
+          if ((pc << 2) < real_vocab) pb[k] = __builtin_nontemporal_load(rowq + pc);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        const int32_t j0 = (p0 + k * kFbThreads) << 2;
+        if (j0 >= padded_vocab) continue;
+        float d[4];
+        dlogits_chunk(pa[k], j0, act, bad, L, g, tgt, real_vocab, d);
+        store_quad(reinterpret_cast<float*>(orow) + j0, d, min(4, padded_vocab - j0));
+      }
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) pa[k] = pb[k];
+    }
+  } else {
+    for (; c0 < n_chunks; c0 += kFbThreads * kFbUnroll) {
+      const int32_t c1 = c0 + kFbThreads * kFbUnroll;
+      if (reread && c1 < n_chunks) {
+#pragma unroll
+        for (int k = 0; k < kFbUnroll; ++k) {
+          const int32_t c = c1 + k * kFbThreads;
+          if ((c << 3) < real_vocab) qb[k] = load_stream(rowp + c);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < kFbUnroll; ++k) {
-        const int32_t c = c1 + k * kFbThreads;
-        if ((c << 3) < real_vocab) qb[k] = load_stream(rowp + c);
+        const int32_t c = c0 + k * kFbThreads;
+        const int32_t j0 = c << 3;
+        if (j0 >= padded_vocab) continue;
+        float d[8];
+        dlogits_chunk(qa[k], j0, act, bad, L, g, tgt, real_vocab, d);
+        Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
       }
-    }
 #pragma unroll
-    for (int k = 0; k < kFbUnroll; ++k) {
-      const int32_t c = c0 + k * kFbThreads;
-      const int32_t j0 = c << 3;
-      if (j0 >= padded_vocab) continue;
-      float d[8];
-      dlogits_chunk(qa[k], j0, act, bad, L, g, tgt, real_vocab, d);
-      Store8<OutT>::store(orow + j0, d, min(8, padded_vocab - j0));
+      for (int k = 0; k < kFbUnroll; ++k) qa[k] = qb[k];
     }
-#pragma unroll
-    for (int k = 0; k < kFbUnroll; ++k) qa[k] = qb[k];
   }
 }
 
