@@ -233,27 +233,33 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
   const int32_t base0 = cf_lo & ~7;
   const int32_t npass = cf_hi > cf_lo ? (cf_hi - base0 + kPassChunks - 1) / kPassChunks : 0;
 
+  // the chunk cut by a tile bound, if this lane has one: its load goes out
+  // first, so that waiting for it does not wait for the passes' loads (the
+  // load counter completes in order)
+  int32_t c = -1, e_lo = 0, e_hi = 0;
+  if (gl == 0 && hi > lo && (lo & 7)) {
+    c = lo >> 3;
+    e_lo = lo & 7;
+    e_hi = min(hi - (c << 3), 8);
+  } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= cf_lo) {
+    c = hi >> 3;
+    e_lo = 0;
+    e_hi = hi & 7;
+  }
+  uint4 qe;
+  if (c >= 0) qe = load_chunk<kNt>(rowp + c);
   uint4 qa[kChunks], qb[kChunks];
-  if (kDepth == 2 && npass > 0) load_pass<kNt>(qa, rowp, base0, cf_lo, cf_hi, gl);
-  {
-    int32_t c = -1, e_lo = 0, e_hi = 0;
-    if (gl == 0 && hi > lo && (lo & 7)) {
-      c = lo >> 3;
-      e_lo = lo & 7;
-      e_hi = min(hi - (c << 3), 8);
-    } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= cf_lo) {
-      c = hi >> 3;
-      e_lo = 0;
-      e_hi = hi & 7;
-    }
-    if (c >= 0) {
-      float v[8];
-      unpack8(load_chunk<kNt>(rowp + c), v);
+  if (kDepth == 2) {
+    if (npass > 0) load_pass<kNt>(qa, rowp, base0, cf_lo, cf_hi, gl);
+    if (npass > 1) load_pass<kNt>(qb, rowp, base0 + kPassChunks, cf_lo, cf_hi, gl);
+  }
+  if (c >= 0) {
+    float v[8];
+    unpack8(qe, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < e_lo || e >= e_hi) v[e] = kNegInf;
-      fold_values<8, kEnt>(v, m, s, a);
-    }
+    for (int e = 0; e < 8; ++e)
+      if (e < e_lo || e >= e_hi) v[e] = kNegInf;
+    fold_values<8, kEnt>(v, m, s, a);
   }
   if (kDepth == 1) {
     for (int32_t p = 0; p < npass; ++p) {
@@ -262,14 +268,14 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
       fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
     }
   } else {
-    // two passes in flight: the next pass's loads are issued before this one folds
+    // two passes in flight: pass p + 2 is issued as soon as pass p has folded
     for (int32_t p = 0; p < npass; p += 2) {
       const int32_t b = base0 + p * kPassChunks;
-      if (p + 1 < npass) load_pass<kNt>(qb, rowp, b + kPassChunks, cf_lo, cf_hi, gl);
       fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
-      if (p + 1 >= npass) break;
       if (p + 2 < npass) load_pass<kNt>(qa, rowp, b + 2 * kPassChunks, cf_lo, cf_hi, gl);
+      if (p + 1 >= npass) break;
       fold_pass<kEnt>(qb, b + kPassChunks, cf_lo, cf_hi, gl, m, s, a);
+      if (p + 3 < npass) load_pass<kNt>(qb, rowp, b + 3 * kPassChunks, cf_lo, cf_hi, gl);
     }
   }
 
