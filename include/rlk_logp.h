@@ -58,6 +58,13 @@
  *     reports them as RLK_ERR_TARGET_RANGE / RLK_ERR_NONFINITE_LSE.
  *   - There is one code path and no fallback: if the GPU path cannot run, the
  *     call fails.
+ *   - Batch size: a dispatch holds its grid size in 32 bits of threads, so a
+ *     large batch is split into several launches of at most 2^31 threads each
+ *     (the backward of 152576-column rows, at 75 blocks of 128 threads per
+ *     row, splits from 223K rows on).  The split never changes a result bit.
+ *     The environment variable RLK_MAX_LAUNCH_THREADS (read at every call;
+ *     values below 1024 count as 1024) lowers the limit, so that tests can
+ *     check this on small inputs.
  */
 #ifndef RLK_LOGP_H_
 #define RLK_LOGP_H_

@@ -321,3 +321,20 @@ def test_extended_forward_and_backward_host_validation():
     rlk.rlk_logp_fwd_ex(desc(num_tokens=0), None, None, None, None, None, None, None, stream=s)
     rlk.rlk_logp_bwd_ex(desc(num_tokens=0), None, None, None, None, None, None, None, None, None,
                         1024, f32, None, stream=s)
+
+
+def test_launch_thread_limit_reads_its_environment_variable(monkeypatch):
+    """The per-launch thread limit (a dispatch's grid size is 32 bits of threads): 2^31 by
+    default, lowered by RLK_MAX_LAUNCH_THREADS (the hook the split-launch GPU test uses),
+    never below 1024 threads, never above 2^31, and a value that is not a number is ignored."""
+    lib = ctypes.CDLL(str(rlk.LIB_PATH))
+    fn = getattr(lib, "_ZN3rlk19launch_thread_limitEv", None)
+    if fn is None:
+        pytest.skip("internal symbol not exported")
+    fn.restype = ctypes.c_int64
+    monkeypatch.delenv("RLK_MAX_LAUNCH_THREADS", raising=False)
+    assert fn() == 1 << 31
+    for value, want in (("5000", 5000), ("10", 1024), (str(1 << 40), 1 << 31), ("abc", 1 << 31),
+                        ("", 1 << 31)):
+        monkeypatch.setenv("RLK_MAX_LAUNCH_THREADS", value)
+        assert fn() == want, value

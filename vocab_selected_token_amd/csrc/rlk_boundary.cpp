@@ -15,6 +15,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <stdlib.h>
 #include <string>
 
 #include "rlk_internal.h"
@@ -592,3 +593,18 @@ const char* rlk_status_string(rlk_status s) {
 const char* rlk_last_error_detail(void) { return g_detail.c_str(); }
 
 }  // extern "C"
+
+namespace rlk {
+
+int64_t launch_thread_limit() {
+  constexpr int64_t kLimit = int64_t{1} << 31;
+  const char* v = getenv("RLK_MAX_LAUNCH_THREADS");
+  if (!v || !*v) return kLimit;
+  char* end = nullptr;
+  const long long n = strtoll(v, &end, 10);
+  if (end == v) return kLimit;  // not a number: the default
+  if (n < 1024) return 1024;    // at least two blocks of every kernel
+  return n < kLimit ? (int64_t)n : kLimit;
+}
+
+}  // namespace rlk

@@ -109,6 +109,14 @@ struct LmheadArgs {
   float* psum;
 };
 
+// Most threads one launch may have.  A dispatch holds its grid size in 32 bits
+// of threads: at 2^32 the launch fails, and above it the size wraps around and
+// the kernel silently runs on a fraction of the grid.  Every launcher splits
+// its work into launches of at most this many threads (2^31, or less when the
+// RLK_MAX_LAUNCH_THREADS environment variable says so -- a hook for tests, which
+// check that any split gives the same bits).
+int64_t launch_thread_limit();
+
 int64_t stage1_blocks(int64_t items);
 int64_t lmhead_grid_blocks(int32_t num_tokens, int32_t real_vocab);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);

@@ -318,23 +318,24 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
 //   pent        [N][T] fp32, the entropy statistic (kEnt only)
 // Work item i = row * tile_count + (tile - tile_begin); group q of wave w of
 // work block b (the XCD-local renumbering of blockIdx.x) takes item
-// 4 (kWPB b + w) + q.  Columns >= V_real never enter the arithmetic; chunks
-// that straddle a tile bound are masked by column index.  kWPB (waves per
-// block) only decides how the waves are packed onto CUs -- one-wave blocks
-// spread a small batch over every CU -- so both launches give the same bits.
+// item_begin + 4 (kWPB b + w) + q, where item_begin > 0 when a large batch
+// takes several launches.  Columns >= V_real never enter the arithmetic;
+// chunks that straddle a tile bound are masked by column index.  Neither kWPB
+// (waves per block: one-wave blocks spread a small batch over every CU) nor the
+// split into launches changes what a tile computes, so all give the same bits.
 // ---------------------------------------------------------------------------
 template <bool kEnt, int kWPB>
 __global__ __launch_bounds__(kWPB * 64) void stage1_partials(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t num_rows, int32_t real_vocab,
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t tile_begin,
-    int32_t tile_count, float* __restrict__ pmax, float* __restrict__ psum,
+    int32_t tile_count, int64_t item_begin, float* __restrict__ pmax, float* __restrict__ psum,
     float* __restrict__ pent) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int gl = lane & 15;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t block = xcd_local_block(blockIdx.x, gridDim.x);
-  const int64_t item0 = (block * kWPB + wave_in_block) * kGroupsPerWave;
+  const int64_t item0 = item_begin + (block * kWPB + wave_in_block) * kGroupsPerWave;
   const int64_t n_items = (int64_t)num_rows * tile_count;
 
   // item -> (row, tile) once per wave on the scalar unit, then step by grp
@@ -652,9 +653,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlogits(
     const uint8_t* __restrict__ mask, int32_t ignore_index, const float* __restrict__ lse,
     const float* __restrict__ grad, const float* __restrict__ grad_lse,
     const float* __restrict__ grad_ent, const float* __restrict__ entropy,
-    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status) {
-  const int32_t row = blockIdx.x / col_blocks;
-  const int32_t cb = blockIdx.x - row * col_blocks;
+    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status,
+    int64_t block_begin) {
+  // block index over the whole batch (a large batch takes several launches)
+  const int64_t gb = block_begin + blockIdx.x;
+  const int32_t row = (int32_t)(gb / col_blocks);
+  const int32_t cb = (int32_t)(gb - (int64_t)row * col_blocks);
   const bool act_mask = (mask == nullptr || mask[row] != 0);
   const int32_t tgt = act_mask ? targets[row] : 0;
   const bool act = act_mask && tgt != ignore_index;
@@ -784,13 +788,13 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width,
     const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
     const float* __restrict__ grad, float* __restrict__ logp, float* __restrict__ lse,
-    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status) {
+    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status, int32_t row_begin) {
   __shared__ float s_m[kFbMaxTiles];
   __shared__ float s_s[kFbMaxTiles];
   __shared__ __align__(16) float s_e[64];
   __shared__ __align__(16) float s_sv[64];
   __shared__ float s_lse;
-  const int32_t row = blockIdx.x;
+  const int32_t row = row_begin + blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave * kGroupsPerWave + (lane >> 4);
@@ -947,21 +951,29 @@ hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
   const int64_t blocks4 = stage1_blocks(items);
   const bool small = blocks4 < kStage1SmallBlocks;
   const int wpb = small ? 1 : kWavesPerBlock;
-  const dim3 grid((unsigned)((items + wpb * kGroupsPerWave - 1) / (wpb * kGroupsPerWave)));
+  const int64_t items_per_block = (int64_t)wpb * kGroupsPerWave;
+  const int64_t blocks = (items + items_per_block - 1) / items_per_block;
+  const int64_t max_blocks = launch_thread_limit() / (wpb * 64);
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {
+    const dim3 grid((unsigned)(blocks - b0 < max_blocks ? blocks - b0 : max_blocks));
+    const int64_t item_begin = b0 * items_per_block;
 #define RLK_LAUNCH_S1(ENT, WPB, PENT)                                                           \
   hipLaunchKernelGGL((stage1_partials<ENT, WPB>), grid, dim3((WPB) * 64), 0, stream, x,       \
                      a.ld / 8, a.num_rows, a.real_vocab, a.padded_vocab, a.num_tiles,         \
-                     a.tile_width, a.tile_begin, a.tile_count, a.pmax, a.psum, PENT)
-  if (a.pent) {
-    if (small) RLK_LAUNCH_S1(true, 1, a.pent);
-    else RLK_LAUNCH_S1(true, kWavesPerBlock, a.pent);
-  } else {
-    if (small) RLK_LAUNCH_S1(false, 1, nullptr);
-    else RLK_LAUNCH_S1(false, kWavesPerBlock, nullptr);
-  }
+                     a.tile_width, a.tile_begin, a.tile_count, item_begin, a.pmax, a.psum, PENT)
+    if (a.pent) {
+      if (small) RLK_LAUNCH_S1(true, 1, a.pent);
+      else RLK_LAUNCH_S1(true, kWavesPerBlock, a.pent);
+    } else {
+      if (small) RLK_LAUNCH_S1(false, 1, nullptr);
+      else RLK_LAUNCH_S1(false, kWavesPerBlock, nullptr);
+    }
 #undef RLK_LAUNCH_S1
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
@@ -988,41 +1000,54 @@ int64_t bwd_col_blocks(int32_t padded_vocab) {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   const int32_t cbs = (int32_t)bwd_col_blocks(a.padded_vocab);
-  const dim3 grid((unsigned)((int64_t)a.num_rows * cbs));
+  const int64_t blocks = (int64_t)a.num_rows * cbs;
+  const int64_t max_blocks = launch_thread_limit() / kBwdThreads;
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
   const bool ex = a.grad_lse || a.grad_ent;
+  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {
+    const dim3 grid((unsigned)(blocks - b0 < max_blocks ? blocks - b0 : max_blocks));
 #define RLK_LAUNCH_BWD(OUT_T, EX)                                                              \
   hipLaunchKernelGGL((bwd_dlogits<OUT_T, EX>), grid, dim3(kBwdThreads), 0, stream, x,         \
                      a.ld / 8, a.num_rows, a.real_vocab, a.padded_vocab, cbs, a.targets,     \
                      a.mask, a.ignore_index, a.lse, a.grad, a.grad_lse, a.grad_ent,          \
-                     a.entropy, reinterpret_cast<OUT_T*>(a.dlogits), a.ld_d, a.status)
-  if (a.out_bf16) {
-    if (ex) RLK_LAUNCH_BWD(uint16_t, true);
-    else RLK_LAUNCH_BWD(uint16_t, false);
-  } else {
-    if (ex) RLK_LAUNCH_BWD(float, true);
-    else RLK_LAUNCH_BWD(float, false);
-  }
+                     a.entropy, reinterpret_cast<OUT_T*>(a.dlogits), a.ld_d, a.status, b0)
+    if (a.out_bf16) {
+      if (ex) RLK_LAUNCH_BWD(uint16_t, true);
+      else RLK_LAUNCH_BWD(uint16_t, false);
+    } else {
+      if (ex) RLK_LAUNCH_BWD(float, true);
+      else RLK_LAUNCH_BWD(float, false);
+    }
 #undef RLK_LAUNCH_BWD
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_fwd_bwd(const FwdBwdArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.num_rows);
+  const int64_t rows_per_launch = launch_thread_limit() / kFbThreads;
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
-  if (a.out_bf16) {
-    hipLaunchKernelGGL(fwd_bwd_rows<uint16_t>, grid, dim3(kFbThreads), 0, stream, x, a.ld / 8,
-                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.targets,
-                       a.mask, a.ignore_index, a.grad, a.logp, a.lse,
-                       reinterpret_cast<uint16_t*>(a.dlogits), a.ld_d, a.status);
-  } else {
-    hipLaunchKernelGGL(fwd_bwd_rows<float>, grid, dim3(kFbThreads), 0, stream, x, a.ld / 8,
-                       a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width, a.targets,
-                       a.mask, a.ignore_index, a.grad, a.logp, a.lse,
-                       reinterpret_cast<float*>(a.dlogits), a.ld_d, a.status);
+  for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
+    const int64_t nr = a.num_rows - r0 < rows_per_launch ? a.num_rows - r0 : rows_per_launch;
+    const dim3 grid((unsigned)nr);
+    const int32_t row_begin = (int32_t)r0;
+    if (a.out_bf16) {
+      hipLaunchKernelGGL(fwd_bwd_rows<uint16_t>, grid, dim3(kFbThreads), 0, stream, x,
+                         a.ld / 8, a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width,
+                         a.targets, a.mask, a.ignore_index, a.grad, a.logp, a.lse,
+                         reinterpret_cast<uint16_t*>(a.dlogits), a.ld_d, a.status, row_begin);
+    } else {
+      hipLaunchKernelGGL(fwd_bwd_rows<float>, grid, dim3(kFbThreads), 0, stream, x,
+                         a.ld / 8, a.real_vocab, a.padded_vocab, a.num_tiles, a.tile_width,
+                         a.targets, a.mask, a.ignore_index, a.grad, a.logp, a.lse,
+                         reinterpret_cast<float*>(a.dlogits), a.ld_d, a.status, row_begin);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_clear_status(uint32_t* status, hipStream_t stream) {

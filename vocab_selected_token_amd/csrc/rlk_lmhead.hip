@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     int32_t num_tokens, int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles,
     int32_t n_vb, int32_t n_tb, const int32_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ seg_m,
-    float* __restrict__ seg_s, float* __restrict__ tlogit) {
+    float* __restrict__ seg_s, float* __restrict__ tlogit, int64_t blk_begin) {
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kSlabBytes];
   static_assert(2 * 2 * kSlabBytes >= kBT * 4 * (int)sizeof(float), "epilogue exchange fits");
 
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   // blocks and each hidden slice by kGroupV, instead of every vocabulary block
   // re-streaming all hidden states.
   constexpr int32_t kGroupV = 4;
-  const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
+  const int64_t blk = blk_begin + xcd_local_block(blockIdx.x, gridDim.x);
   const int64_t strip = blk / ((int64_t)kGroupV * n_tb);
   const int32_t r_in = (int32_t)(blk - strip * kGroupV * n_tb);
   const int32_t strip_w = min(kGroupV, n_vb - (int32_t)strip * kGroupV);  // last strip may be narrow
@@ -405,8 +405,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 __global__ __launch_bounds__(256) void lmhead_tiles(
     const float* __restrict__ seg_m, const float* __restrict__ seg_s, int32_t num_tokens,
     int32_t n_vb, int32_t padded_vocab, int32_t num_tiles, float* __restrict__ pmax,
-    float* __restrict__ psum) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float* __restrict__ psum, int64_t idx_begin) {
+  const int64_t idx = idx_begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)num_tokens * num_tiles) return;
   const int32_t tok = (int32_t)(idx / num_tiles);
   const int32_t t = (int32_t)(idx - (int64_t)tok * num_tiles);
@@ -446,18 +446,32 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   const int32_t n_vb = (a.real_vocab + kBV - 1) / kBV;
   const int32_t n_tb = (a.num_tokens + kBT - 1) / kBT;
-  hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)((int64_t)n_vb * n_tb)), dim3(kThreads), 0,
-                     stream, reinterpret_cast<const u32x4*>(a.hidden),
-                     reinterpret_cast<const u32x4*>(a.weight), a.hidden_dim, a.num_tokens,
-                     a.real_vocab, a.padded_vocab, a.num_tiles, n_vb, n_tb, a.targets, a.mask,
-                     a.ignore_index, a.seg_m, a.seg_s, a.target_logit);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int64_t limit = launch_thread_limit();
+  // the GEMM blocks in launches of at most limit / kThreads blocks; a block's
+  // work index (and so its tile) does not depend on the split
+  const int64_t blocks = (int64_t)n_vb * n_tb;
+  const int64_t max_blocks = limit / kThreads;
+  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {
+    const int64_t nb = blocks - b0 < max_blocks ? blocks - b0 : max_blocks;
+    hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)nb), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const u32x4*>(a.hidden),
+                       reinterpret_cast<const u32x4*>(a.weight), a.hidden_dim, a.num_tokens,
+                       a.real_vocab, a.padded_vocab, a.num_tiles, n_vb, n_tb, a.targets, a.mask,
+                       a.ignore_index, a.seg_m, a.seg_s, a.target_logit, b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t items = (int64_t)a.num_tokens * a.num_tiles;
-  hipLaunchKernelGGL(lmhead_tiles, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
-                     a.seg_m, a.seg_s, a.num_tokens, n_vb, a.padded_vocab, a.num_tiles, a.pmax,
-                     a.psum);
-  return hipGetLastError();
+  const int64_t max_items = limit / 256 * 256;
+  for (int64_t i0 = 0; i0 < items; i0 += max_items) {
+    const int64_t ni = items - i0 < max_items ? items - i0 : max_items;
+    hipLaunchKernelGGL(lmhead_tiles, dim3((unsigned)((ni + 255) / 256)), dim3(256), 0, stream,
+                       a.seg_m, a.seg_s, a.num_tokens, n_vb, a.padded_vocab, a.num_tiles, a.pmax,
+                       a.psum, i0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace rlk
