@@ -338,3 +338,42 @@ def test_launch_thread_limit_reads_its_environment_variable(monkeypatch):
                         ("", 1 << 31)):
         monkeypatch.setenv("RLK_MAX_LAUNCH_THREADS", value)
         assert fn() == want, value
+
+
+def test_conveniences_check_tensors_before_anything_runs():
+    """The torch conveniences check each tensor's shape, dtype and device before calling the
+    C entry points, which take bare pointers and cannot see dtypes (an int64 targets tensor
+    would be read as pairs of int32 words)."""
+    import torch
+
+    n, v = 6, 40
+    x = torch.zeros(n, v, dtype=torch.bfloat16)
+    t32 = torch.zeros(n, dtype=torch.int32)
+    g = torch.zeros(n)
+    kw = dict(real_vocab=v, num_vocab_tiles=4)
+    with pytest.raises(TypeError, match="int32"):
+        rlk.forward(x, t32.long(), **kw)
+    with pytest.raises(TypeError, match="bfloat16"):
+        rlk.forward(x.float(), t32, **kw)
+    with pytest.raises(ValueError, match="6 elements"):
+        rlk.forward(x, t32[:5], **kw)
+    with pytest.raises(ValueError, match="unit column stride"):
+        rlk.forward(x.t(), t32, **kw)
+    with pytest.raises(TypeError, match="active_mask"):
+        rlk.forward(x, t32, torch.ones(n, dtype=torch.int32), **kw)
+    with pytest.raises(TypeError, match="grad_logp"):
+        rlk.backward(x, t32, None, g, g.double(), **kw)
+    with pytest.raises(ValueError, match="contiguous"):
+        rlk.backward(x, t32, None, torch.zeros(2 * n)[::2], g, **kw)
+    with pytest.raises(TypeError, match="grad_logp"):
+        rlk.forward_backward(x, t32, None, None, **kw)
+    with pytest.raises(ValueError, match="GPU memory"):
+        rlk.forward(x, t32, **kw)
+    with pytest.raises(ValueError, match="columns"):
+        rlk.fused_lmhead(torch.zeros(n, 64, dtype=torch.bfloat16),
+                         torch.zeros(v, 128, dtype=torch.bfloat16), t32, real_vocab=v)
+    with pytest.raises(ValueError, match="rows"):
+        rlk.fused_lmhead(torch.zeros(n, 64, dtype=torch.bfloat16),
+                         torch.zeros(v - 1, 64, dtype=torch.bfloat16), t32, real_vocab=v)
+    with pytest.raises(TypeError, match="int32"):
+        rlk.selected_token_logprob(x, t32.long(), real_vocab=v, num_vocab_tiles=4)

@@ -204,6 +204,63 @@ def rlk_last_error_detail() -> str:
 
 
 # -- conveniences: allocate outputs with torch, then call the C entry points ----
+# The C entry points take bare pointers and cannot see dtypes, so the conveniences
+# check every tensor first (shape and dtype, then device) and raise before anything
+# is enqueued.  Targets must already be int32: an int64 tensor would be read as
+# pairs of int32 words, and narrowing it here could turn an out-of-range target
+# into a valid column.
+def _check_logits(logits, name="logits"):
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    if logits.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {logits.dtype}")
+    if logits.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+
+
+def _check_rows(name, t, n, dtypes):
+    """A per-row vector: 1-D, n elements, contiguous, of one of `dtypes`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        hint = " (convert with .to(torch.int32))" if name == "targets" else ""
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, "
+                        f"got {t.dtype}{hint}")
+    if t.dim() != 1 or t.numel() != n:
+        raise ValueError(f"{name} must be 1-D with {n} elements, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(base, **tensors):
+    if base.device.type != "cuda":
+        raise ValueError(f"the inputs must be in GPU memory, got {base.device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != base.device:
+            raise ValueError(f"{name} is on {t.device}, the logits on {base.device}")
+
+
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_MASK = (torch.uint8, torch.bool)
+
+
+def _check_inputs(logits, targets, active_mask, **vectors):
+    """logits bf16 [N, ld]; targets int32 [N]; mask uint8/bool [N] or None; every other
+    keyword an fp32 [N] vector or None.  All on the logits' GPU."""
+    _check_logits(logits)
+    n = logits.shape[0]
+    _check_rows("targets", targets, n, _I32)
+    if targets is None:
+        raise TypeError("targets must be a torch.Tensor")
+    _check_rows("active_mask", active_mask, n, _MASK)
+    for name, t in vectors.items():
+        _check_rows(name, t, n, _F32)
+    _check_device(logits, targets=targets, active_mask=active_mask, **vectors)
+
+
 def _u8_mask(mask):
     if mask is None:
         return None
@@ -222,6 +279,7 @@ def forward(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *, re
             num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
             workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse), fp32 [N] each.  logits: bf16 [N, ld] with unit column stride."""
+    _check_inputs(logits, targets, active_mask)
     n = logits.shape[0]
     desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
                      num_vocab_tiles, num_virtual_shards, ignore_index, validate)
@@ -241,6 +299,7 @@ def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torc
     """dlogits [N, V_pad] (fp32 or bf16)."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    _check_inputs(logits, targets, active_mask, lse=lse, grad_logp=grad_logp)
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
     tiles = num_vocab_tiles if num_vocab_tiles is not None else min(64, v_pad)
@@ -260,6 +319,7 @@ def forward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *,
                num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
                workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse, entropy), fp32 [N] each."""
+    _check_inputs(logits, targets, active_mask)
     n = logits.shape[0]
     desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
                      num_vocab_tiles, num_virtual_shards, ignore_index, validate)
@@ -285,6 +345,8 @@ def backward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: t
     """dlogits [N, V_pad] of a loss on (logp, lse, entropy); absent gradients are zero."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    _check_inputs(logits, targets, active_mask, lse=lse, entropy=entropy, grad_logp=grad_logp,
+                  grad_lse=grad_lse, grad_ent=grad_ent)
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
     tiles = num_vocab_tiles if num_vocab_tiles is not None else min(64, v_pad)
@@ -346,8 +408,7 @@ def selected_token_logprob(logits: torch.Tensor, targets: torch.Tensor, active_m
     autograd hands the three upstream gradients to rlk_logp_bwd_ex.  logits is
     bf16 [N, ld] with unit column stride; its gradient has its dtype.
     """
-    if logits.dim() != 2 or logits.stride(1) != 1 or logits.dtype != torch.bfloat16:
-        raise ValueError("logits must be a 2-D bf16 tensor with unit column stride")
+    _check_inputs(logits, targets, active_mask)
     return _SelectedTokenLogprob.apply(logits, targets, active_mask, real_vocab, padded_vocab,
                                        num_vocab_tiles, ignore_index)
 
@@ -360,6 +421,9 @@ def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,
     """(logp, lse, dlogits [N, V_pad]) in one launch, with g known up front."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    if grad_logp is None:
+        raise TypeError("grad_logp must be a torch.Tensor")
+    _check_inputs(logits, targets, active_mask, grad_logp=grad_logp)
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
     desc = make_desc(n, real_vocab, v_pad, logits.stride(0), num_vocab_tiles, num_virtual_shards,
@@ -385,6 +449,20 @@ def fused_lmhead(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tens
                  workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse) of z = hidden . weight^T without materialising z.
     hidden: bf16 [N, K] contiguous; weight: bf16 [V_pad, K] contiguous."""
+    for name, t in (("hidden", hidden), ("weight", weight)):
+        _check_logits(t, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if weight.shape[1] != hidden.shape[1]:
+        raise ValueError(f"weight has {weight.shape[1]} columns, hidden {hidden.shape[1]}")
+    if weight.shape[0] < real_vocab:
+        raise ValueError(f"weight has {weight.shape[0]} rows, fewer than real_vocab={real_vocab}")
+    n = hidden.shape[0]
+    _check_rows("targets", targets, n, _I32)
+    if targets is None:
+        raise TypeError("targets must be a torch.Tensor")
+    _check_rows("active_mask", active_mask, n, _MASK)
+    _check_device(hidden, weight=weight, targets=targets, active_mask=active_mask)
     n, k = hidden.shape
     v_pad = padded_vocab or weight.shape[0]
     desc = make_desc(n, real_vocab, v_pad, v_pad, num_vocab_tiles, 1, ignore_index, validate)
