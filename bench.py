@@ -208,7 +208,7 @@ def main() -> int:
                     help="also run an untimed plain copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-device by design", file=sys.stderr)
         return 2
 
