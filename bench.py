@@ -301,7 +301,13 @@ def main() -> int:
     ms_step = (t1 - t0) * 1e3 / args.steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if wl.backward else 0.0
-    log(f"bench: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms)")
+    # spread of the individual steps as the stream saw them (events around each step)
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    pick = lambda q: per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
+    step_spread = {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4),
+                   "p90": round(pick(0.9), 4)}
+    log(f"bench: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms; "
+        f"step p10/p50/p90 {step_spread['p10']}/{step_spread['p50']}/{step_spread['p90']} ms)")
 
     if args.copy_probe_gib > 0:  # plain copy kernel of known size, for counter scaling
         nbytes = int(args.copy_probe_gib * 2 ** 30)
@@ -364,6 +370,7 @@ def main() -> int:
                    else ("rlk_logp_fwd_ex then rlk_logp_bwd_ex (entropy; logp, LSE and entropy "
                          "gradients)" if extended else "rlk_logp_fwd then rlk_logp_bwd")},
         "tokens_per_s": round(n / (ms_step * 1e-3), 1),
+        "step_ms_stream": step_spread,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": total_bytes,
         "kernels": kernels,
