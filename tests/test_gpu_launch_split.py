@@ -34,6 +34,9 @@ def run_all(inp, wl, lm):
     out["fwd_s4"] = rlk.forward(inp.logits, inp.targets, inp.mask, num_virtual_shards=4, **kw)
     logp, lse, ent = rlk.forward_ex(inp.logits, inp.targets, inp.mask, **kw)
     out["fwd_ex"] = (logp, lse, ent)
+    # 16 tiles per shard: stage 1 takes its one-wave-block form
+    out["fwd_ex_s4"] = rlk.forward_ex(inp.logits, inp.targets, inp.mask, num_virtual_shards=4,
+                                      **kw)
     for dt in (torch.float32, torch.bfloat16):
         out[f"bwd_{dt}"] = (rlk.backward(inp.logits, inp.targets, inp.mask, lse, inp.grad,
                                          out_dtype=dt, **kw),)
