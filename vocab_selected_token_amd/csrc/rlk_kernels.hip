@@ -369,6 +369,16 @@ __global__ __launch_bounds__(kWPB * 64) void stage1_partials(
 constexpr int kMergeThreads = 64;  // one row per lane; small blocks spread rows over every CU
 constexpr int kMergeVec = 64;      // tiles held in registers by the vectorised path
 
+// The merge accumulates S = sum_t s_t exp(m_t - M) in fp64, in ascending tile
+// order: a running fp32 sum of T terms drifts by up to T half-ulps, which at
+// T = 1024 tiles moves LSE by a few 1e-6 and an fp32 dX entry g (1 - p) by about
+// 1e-5.  The exponentials are fp32 (each term's own error averages out) and
+// s_t exp(m_t - M) is exact in fp64.  LSE = M + log S is formed in fp64 and
+// rounded to fp32 once.
+__device__ __forceinline__ float lse_of(float M, double S) {
+  return (float)((double)M + log(S));
+}
+
 // LSE from a row's T partials: exact max first, then the rescaled sum in
 // ascending tile order with fmaf, skipping identity partials; -inf if every
 // partial is the identity.  pm/ps point at the row's T values.
@@ -391,34 +401,35 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
     for (int t = 0; t < kMergeVec; ++t)
       if (t < num_tiles) M = maxnan(M, mv[t]);
     if (M == kNegInf) return kNegInf;
-    float S = 0.0f;
+    double S = 0.0;
 #pragma unroll
     for (int t = 0; t < kMergeVec; ++t)
-      if (t < num_tiles && mv[t] != kNegInf) S = fmaf(sv[t], expf(mv[t] - M), S);
-    return M + logf(S);
+      if (t < num_tiles && mv[t] != kNegInf) S = fma((double)sv[t], (double)expf(mv[t] - M), S);
+    return lse_of(M, S);
   }
   float M = kNegInf;
   for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
   if (M == kNegInf) return kNegInf;
-  float S = 0.0f;
+  double S = 0.0;
   for (int32_t t = 0; t < num_tiles; ++t) {
     const float mt = pm[t];
-    if (mt != kNegInf) S = fmaf(ps[t], expf(mt - M), S);
+    if (mt != kNegInf) S = fma((double)ps[t], (double)expf(mt - M), S);
   }
-  return M + logf(S);
+  return lse_of(M, S);
 }
 
 // merge_row's arithmetic plus the entropy: alongside S it accumulates, in the
-// same ascending order, A = sum_t exp(m_t - M) (a_t + (m_t - M) s_t), which is
-// sum_j exp(x_j - M) (x_j - M) over the row.  Then LSE = M + log S (the same
-// bits as merge_row) and H = log S - A / S; H is NaN where LSE is not finite
-// (no distribution).
+// same ascending order and also in fp64, A = sum_t exp(m_t - M) (a_t + (m_t - M)
+// s_t), which is sum_j exp(x_j - M) (x_j - M) over the row.  Then LSE = M + log S
+// (the same bits as merge_row) and H = log S - A / S, rounded to fp32 once; H is
+// NaN where LSE is not finite (no distribution).
 __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
                                                    const float* __restrict__ ps,
                                                    const float* __restrict__ pa,
                                                    int32_t num_tiles, float& H) {
   H = __builtin_nanf("");
-  float M = kNegInf, S = 0.0f, A = 0.0f;
+  float M = kNegInf;
+  double S = 0.0, A = 0.0;
   if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
     // same arithmetic, with the loads issued up front as 16-byte vectors
     float mv[kMergeVec], sv[kMergeVec], av[kMergeVec];
@@ -440,9 +451,10 @@ __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
 #pragma unroll
     for (int t = 0; t < kMergeVec; ++t) {
       if (t < num_tiles && mv[t] != kNegInf) {
-        const float e = expf(mv[t] - M);
-        S = fmaf(sv[t], e, S);
-        A = fmaf(e, fmaf(mv[t] - M, sv[t], av[t]), A);
+        const float d = mv[t] - M;
+        const double e = (double)expf(d);
+        S = fma((double)sv[t], e, S);
+        A = fma(e, fma((double)d, (double)sv[t], (double)av[t]), A);
       }
     }
   } else {
@@ -451,15 +463,15 @@ __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
     for (int32_t t = 0; t < num_tiles; ++t) {
       const float mt = pm[t];
       if (mt != kNegInf) {
-        const float e = expf(mt - M);
-        S = fmaf(ps[t], e, S);
-        A = fmaf(e, fmaf(mt - M, ps[t], pa[t]), A);
+        const float d = mt - M;
+        const double e = (double)expf(d);
+        S = fma((double)ps[t], e, S);
+        A = fma(e, fma((double)d, (double)ps[t], (double)pa[t]), A);
       }
     }
   }
-  const float lS = logf(S);
-  const float L = M + lS;
-  if (__builtin_isfinite(L)) H = lS - A / S;
+  const float L = lse_of(M, S);
+  if (__builtin_isfinite(L)) H = (float)(log(S) - A / S);
   return L;
 }
 
@@ -754,9 +766,9 @@ constexpr int kFbUnroll = 4;
 // The stage-2 merge of T <= 64 partials held one per lane of a wave (lane t
 // holds tile t; lanes >= T hold the identity).  The max is exact in any order
 // and the exponentials are taken in parallel; the fmaf chain then runs in
-// ascending tile order over LDS copies, as in merge_row.  An identity partial
-// enters the chain as fmaf(0, 0, S), which is S (S >= +0), exactly as if it
-// were skipped.  Every lane returns the LSE.
+// ascending tile order over LDS copies, in fp64 as in merge_row.  An identity
+// partial enters the chain as fma(0, 0, S), which is S (S >= +0), exactly as if
+// it were skipped.  Every lane returns the LSE.
 __device__ __forceinline__ float merge_lanes(float mt, float st, int32_t num_tiles, int lane,
                                              float* s_e, float* s_sv) {
   float M = mt;
@@ -769,17 +781,17 @@ __device__ __forceinline__ float merge_lanes(float mt, float st, int32_t num_til
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float S = 0.0f;
+  double S = 0.0;
 #pragma unroll
   for (int t = 0; t < 64; t += 4) {
     const float4 e4 = *reinterpret_cast<const float4*>(s_e + t);
     const float4 s4 = *reinterpret_cast<const float4*>(s_sv + t);
-    S = fmaf(s4.x, e4.x, S);
-    S = fmaf(s4.y, e4.y, S);
-    S = fmaf(s4.z, e4.z, S);
-    S = fmaf(s4.w, e4.w, S);
+    S = fma((double)s4.x, (double)e4.x, S);
+    S = fma((double)s4.y, (double)e4.y, S);
+    S = fma((double)s4.z, (double)e4.z, S);
+    S = fma((double)s4.w, (double)e4.w, S);
   }
-  return M + logf(S);
+  return lse_of(M, S);
 }
 
 template <typename OutT>
