@@ -134,7 +134,7 @@ def bench_lmhead(args) -> int:
     h = torch.randn((n, k), generator=g, device=dev).to(torch.bfloat16)
     w = (torch.randn((v_pad, k), generator=g, device=dev) * 0.02).to(torch.bfloat16)
     tgt = torch.randint(0, v_real, (n,), generator=g, device=dev, dtype=torch.int32)
-    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, 1, -100)
+    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, args.shards, -100)
     ws = torch.empty(rlk.rlk_logp_fused_lmhead_workspace_bytes(desc), dtype=torch.uint8,
                      device=dev)
     logp = torch.empty(n, device=dev)
@@ -174,7 +174,8 @@ def bench_lmhead(args) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": LMHEAD_WORKLOAD, "tokens": n, "hidden": k, "real_vocab": v_real,
-                   "padded_vocab": v_pad, "vocab_tiles": tiles},
+                   "padded_vocab": v_pad, "vocab_tiles": tiles,
+                   "virtual_shards": args.shards},
         "tokens_per_s": round(n / (ev_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -248,9 +248,14 @@ rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
  * and LSE -- with the statistics and the target logit read from the fp32
  * accumulators (no rounding of z to bf16).
  *   desc        num_tokens, real_vocab, padded_vocab, num_vocab_tiles,
- *               ignore_index and flags as for rlk_logp_fwd; ld_logits is not
- *               used; num_virtual_shards must be 1; every tile must be at least
- *               256 columns wide (padded_vocab / num_vocab_tiles >= 256).
+ *               num_virtual_shards, ignore_index and flags as for rlk_logp_fwd;
+ *               ld_logits is not used; every tile must be at least 256 columns
+ *               wide (padded_vocab / num_vocab_tiles >= 256).  Each virtual
+ *               shard is computed by its own launches over its own weight rows
+ *               only, as one GPU of a vocabulary-parallel LM head would be; logp,
+ *               LSE and the per-tile partials are bitwise the same for every
+ *               num_virtual_shards in [1, num_vocab_tiles] ([PR289] PR1:
+ *               tile-aligned vocabulary shards, fixed-order merge).
  *   hidden      (device) bf16 [num_tokens, hidden_dim], row-major, 16-byte aligned.
  *   weight      (device) bf16 [padded_vocab, hidden_dim], row-major, 16-byte
  *               aligned; rows >= real_vocab are never read.
@@ -260,7 +265,7 @@ rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
  *               aligned.  Its status words and per-tile partials sit where
  *               rlk_logp_fwd puts them; the rest is scratch.
  * Errors as for rlk_logp_fwd; RLK_ERR_BAD_TILING also for tiles narrower than
- * 256 columns or num_virtual_shards != 1. */
+ * 256 columns. */
 size_t rlk_logp_fused_lmhead_workspace_bytes(const rlk_logp_desc* desc);
 rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
                                  const void* weight, int64_t hidden_dim, const int32_t* targets,

@@ -48,6 +48,8 @@ def run_all(inp, wl, lm):
     h, w, tg, v_real, v_pad, t = lm
     out["lmhead"] = rlk.fused_lmhead(h, w, tg, real_vocab=v_real, padded_vocab=v_pad,
                                      num_vocab_tiles=t)
+    out["lmhead_s3"] = rlk.fused_lmhead(h, w, tg, real_vocab=v_real, padded_vocab=v_pad,
+                                        num_vocab_tiles=t, num_virtual_shards=3)
     torch.cuda.synchronize()
     return {k: tuple(bits(x).cpu() for x in v) for k, v in out.items()}
 
@@ -72,6 +74,8 @@ def test_split_launches_give_the_same_bits(case, limit, monkeypatch):
     print(f"launch limit {limit} threads", flush=True)
     monkeypatch.setenv("RLK_MAX_LAUNCH_THREADS", str(limit))
     got = run_all(inp, wl, lm)
+    for a, b in zip(ref["lmhead"], got["lmhead_s3"]):
+        assert torch.equal(a, b), "three virtual shards differ from one"
     for key in ref:
         for a, b in zip(ref[key], got[key]):
             assert torch.equal(a, b), f"{key} differs with a {limit}-thread launch limit"

@@ -32,9 +32,9 @@ def make_case(n, k, v_real, v_pad, seed, w_sigma=0.05, mask_keep=0.8, ignore_fra
     return h, w, tgt, mask
 
 
-def run(h, w, tgt, mask, v_real, v_pad, tiles, validate=False):
+def run(h, w, tgt, mask, v_real, v_pad, tiles, validate=False, shards=1):
     n, k = h.shape
-    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, 1, IGNORE, validate)
+    desc = rlk.make_desc(n, v_real, v_pad, v_pad, tiles, shards, IGNORE, validate)
     ws = torch.empty(rlk.rlk_logp_fused_lmhead_workspace_bytes(desc), dtype=torch.uint8,
                      device=DEV)
     logp = torch.empty(n, device=DEV)
@@ -99,6 +99,65 @@ def test_fused_small_parity(c):
     assert np.max(np.abs(rec[act] - ztg[act])) <= 1e-4
 
 
+def partials(ws, n, t):
+    """The per-tile (max, sumexp) the fused call leaves in its workspace, as int32 bits."""
+    part = (n * t * 4 + 255) // 256 * 256
+    return (ws[256:256 + n * t * 4].view(torch.int32).cpu(),
+            ws[256 + part:256 + part + n * t * 4].view(torch.int32).cpu())
+
+
+SHARD_CASES = [
+    # 320-column tiles: most shard bounds cut a 256-column GEMM block
+    dict(n=300, k=128, v_real=5000, v_pad=5120, tiles=16, shards=[2, 3, 4, 5, 7, 8, 16]),
+    # 256-column tiles, real columns end in tile 2: shards of padding only
+    dict(n=37, k=64, v_real=700, v_pad=4096, tiles=16, shards=[2, 4, 8, 16]),
+    # 428/429-column tiles; the real columns end inside the block a shard bound cuts
+    dict(n=257, k=192, v_real=2900, v_pad=3000, tiles=7, shards=[2, 3, 7]),
+    # 2384-column tiles as in the 152576-column vocabulary, at a small scale
+    dict(n=65, k=64, v_real=18500, v_pad=19072, tiles=8, shards=[2, 4, 8]),
+]
+
+
+@pytest.mark.parametrize("c", SHARD_CASES,
+                         ids=lambda c: "n{n}_k{k}_v{v_real}_p{v_pad}_T{tiles}".format(**c))
+def test_fused_virtual_shards_bitwise(c):
+    """Any grouping of the tiles into virtual shards gives the same bits: logp, LSE
+    and every per-tile partial.  Each shard's launches read only its own weight rows
+    (the rest hold garbage here), and the result still matches the oracle."""
+    print(f"case {c}", flush=True)
+    n, t = c["n"], c["tiles"]
+    h, w, tgt, mask = make_case(n, c["k"], c["v_real"], c["v_pad"], seed=n + 1000)
+    ref = run(h, w, tgt, mask, c["v_real"], c["v_pad"], t)
+    ref_bits = (ref[0].view(torch.int32).cpu(), ref[1].view(torch.int32).cpu()) + \
+        partials(ref[2], n, t)
+    bounds = [(i * c["v_pad"]) // t for i in range(t + 1)]
+    for s in c["shards"]:
+        got = run(h, w, tgt, mask, c["v_real"], c["v_pad"], t, shards=s)
+        got_bits = (got[0].view(torch.int32).cpu(), got[1].view(torch.int32).cpu()) + \
+            partials(got[2], n, t)
+        for name, a, b in zip(("logp", "lse", "pmax", "psum"), ref_bits, got_bits):
+            assert torch.equal(a, b), f"{name} differs at S={s}"
+        # the shard that owns the last real column ends there: spoil every weight row
+        # past the first shard and check that shard 0's partials do not move
+        first_end = bounds[t // s]
+        if first_end < c["v_real"]:
+            w2 = w.clone()
+            w2[first_end:] = torch.randint(-32768, 32768, w2[first_end:].shape, device=DEV,
+                                           dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+            spoiled = run(h, w2, tgt, mask, c["v_real"], c["v_pad"], t, shards=s)
+            pm_a, ps_a = partials(got[2], n, t)
+            pm_b, ps_b = partials(spoiled[2], n, t)
+            k0 = t // s  # tiles of shard 0
+            assert torch.equal(pm_a.view(n, t)[:, :k0], pm_b.view(n, t)[:, :k0])
+            assert torch.equal(ps_a.view(n, t)[:, :k0], ps_b.view(n, t)[:, :k0])
+    o = oracle.get()
+    z = o.lmhead_logits(bf16_bits(h), bf16_bits(w), real_vocab=c["v_real"])
+    t_h, m_h = tgt.cpu().numpy(), mask.cpu().numpy()
+    lo, so, _, _ = o.fwd(z, t_h, m_h, real_vocab=c["v_real"])
+    P.check_fwd(ref[0].cpu().numpy(), ref[1].cpu().numpy(), lo, so,
+                P.effective_active(t_h, m_h), str(c))
+
+
 def test_fused_repeat_and_batch_invariance():
     h, w, tgt, mask = make_case(300, 128, 2500, 2560, seed=3)
     a = run(h, w, tgt, mask, 2500, 2560, 10)
@@ -140,3 +199,8 @@ def test_fused_lmhead_4096_sampled():
     stats = P.check_fwd(logp.cpu().numpy()[rows], lse.cpu().numpy()[rows], lo, so,
                         np.ones(len(rows), bool), "lmhead 4096")
     print(stats, flush=True)
+    # the 64 tiles grouped into 2, 4 and 8 virtual shards: the same bits
+    for s in (2, 4, 8):
+        lp_s, lse_s, _ = run(h, w, tgt, None, v_real, v_pad, 64, shards=s)
+        assert torch.equal(lp_s.view(torch.int32), logp.view(torch.int32)), s
+        assert torch.equal(lse_s.view(torch.int32), lse.view(torch.int32)), s

@@ -222,7 +222,9 @@ def test_fused_lmhead_host_validation():
         (desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=5), 64,
          rlk.RLK_ERR_BAD_TILING),  # tiles narrower than 256 columns
         (desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=4,
-              num_virtual_shards=2), 64, rlk.RLK_ERR_BAD_TILING),
+              num_virtual_shards=5), 64, rlk.RLK_ERR_BAD_TILING),  # more shards than tiles
+        (desc(num_tokens=8, real_vocab=1000, padded_vocab=1024, num_vocab_tiles=4,
+              num_virtual_shards=0), 64, rlk.RLK_ERR_BAD_TILING),
         (ok, 96, rlk.RLK_ERR_BAD_SHAPE),  # hidden_dim not a multiple of 64
         (ok, 0, rlk.RLK_ERR_BAD_SHAPE),
     ]

@@ -445,7 +445,8 @@ def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,
 
 def fused_lmhead(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                  active_mask=None, *, real_vocab: int, padded_vocab: int | None = None,
-                 num_vocab_tiles: int = 64, ignore_index: int = -100, validate: bool = False,
+                 num_vocab_tiles: int = 64, num_virtual_shards: int = 1,
+                 ignore_index: int = -100, validate: bool = False,
                  workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse) of z = hidden . weight^T without materialising z.
     hidden: bf16 [N, K] contiguous; weight: bf16 [V_pad, K] contiguous."""
@@ -465,7 +466,8 @@ def fused_lmhead(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tens
     _check_device(hidden, weight=weight, targets=targets, active_mask=active_mask)
     n, k = hidden.shape
     v_pad = padded_vocab or weight.shape[0]
-    desc = make_desc(n, real_vocab, v_pad, v_pad, num_vocab_tiles, 1, ignore_index, validate)
+    desc = make_desc(n, real_vocab, v_pad, v_pad, num_vocab_tiles, num_virtual_shards,
+                     ignore_index, validate)
     logp = torch.empty(n, dtype=torch.float32, device=hidden.device)
     lse = torch.empty(n, dtype=torch.float32, device=hidden.device)
     if workspace is None:

@@ -459,9 +459,9 @@ rlk_status check_fused_desc(const rlk_logp_desc* d) {
                 "fused LM-head needs tiles of at least %d columns (padded_vocab / "
                 "num_vocab_tiles = %lld)",
                 rlk::kLmheadBlockVocab, (long long)(d->padded_vocab / d->num_vocab_tiles));
-  if (d->num_virtual_shards != 1)
-    return fail(RLK_ERR_BAD_TILING, "fused LM-head takes num_virtual_shards = 1 (got %d)",
-                d->num_virtual_shards);
+  if (d->num_virtual_shards < 1 || d->num_virtual_shards > d->num_vocab_tiles)
+    return fail(RLK_ERR_BAD_TILING, "num_virtual_shards=%d outside [1, num_vocab_tiles=%d]",
+                d->num_virtual_shards, d->num_vocab_tiles);
   if (d->flags & ~RLK_FLAG_VALIDATE)
     return fail(RLK_ERR_BAD_SHAPE, "unknown flag bits 0x%x", d->flags & ~RLK_FLAG_VALIDATE);
   return RLK_OK;
@@ -541,6 +541,7 @@ rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
   a.real_vocab = (int32_t)desc->real_vocab;
   a.padded_vocab = (int32_t)desc->padded_vocab;
   a.num_tiles = desc->num_vocab_tiles;
+  a.num_shards = desc->num_virtual_shards;
   a.targets = targets;
   a.mask = active_mask;
   a.ignore_index = desc->ignore_index;

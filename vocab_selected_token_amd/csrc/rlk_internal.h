@@ -99,6 +99,7 @@ struct LmheadArgs {
   int32_t real_vocab;
   int32_t padded_vocab;
   int32_t num_tiles;
+  int32_t num_shards;  // virtual shards: launched one after another
   const int32_t* targets;
   const uint8_t* mask;  // may be null
   int32_t ignore_index;

@@ -110,17 +110,26 @@ __device__ __forceinline__ int32_t inner_tile_bound(int32_t v0, int32_t padded_v
 // ---------------------------------------------------------------------------
 // lmhead_segments
 //   h          bf16 [num_tokens, K] (16-byte chunks, K/8 per row)
-//   w          bf16 [>= real_vocab, K]; rows >= real_vocab are never read
+//   w          bf16 [>= real_vocab, K]; only rows [row_lo, row_hi) are read
 //   seg_m/s    [num_tokens][2 * n_vb]: slot 2*vb holds the block's columns
 //              before its inner tile bound (all of them if there is none), slot
 //              2*vb+1 those from the bound on ((-inf, 0) if there is none)
 //   tlogit     [num_tokens] fp32 target logit, written for effective-active
-//              tokens whose target is a real column of this block
+//              tokens whose target is a column of this block in [row_lo, row_hi)
+// One launch covers one virtual shard: the vocabulary blocks vb_begin ..
+// vb_begin + n_vbs - 1 of the global 256-column block grid that overlap the
+// shard's real columns [row_lo, row_hi).  Rows outside that range are neither
+// read nor counted, and a segment slot is written only by the shard whose
+// columns [col_lo, col_hi) hold the slot's first column.  A segment lies
+// inside one tile, so it holds the same rows, summed in the same order, under
+// every grouping of the tiles: the slots, and so the partials, do not depend
+// on the shard count.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void lmhead_segments(
     const u32x4* __restrict__ h, const u32x4* __restrict__ w, int32_t hidden_dim,
-    int32_t num_tokens, int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles,
-    int32_t n_vb, int32_t n_tb, const int32_t* __restrict__ targets,
+    int32_t num_tokens, int32_t padded_vocab, int32_t num_tiles,
+    int32_t n_vb, int32_t n_tb, int32_t vb_begin, int32_t n_vbs, int32_t row_lo,
+    int32_t row_hi, int32_t col_lo, int32_t col_hi, const int32_t* __restrict__ targets,
     const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ seg_m,
     float* __restrict__ seg_s, float* __restrict__ tlogit, int64_t blk_begin) {
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kSlabBytes];
@@ -143,8 +152,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int64_t blk = blk_begin + xcd_local_block(blockIdx.x, gridDim.x);
   const int64_t strip = blk / ((int64_t)kGroupV * n_tb);
   const int32_t r_in = (int32_t)(blk - strip * kGroupV * n_tb);
-  const int32_t strip_w = min(kGroupV, n_vb - (int32_t)strip * kGroupV);  // last strip may be narrow
-  const int32_t vb = (int32_t)strip * kGroupV + r_in % strip_w;
+  const int32_t strip_w = min(kGroupV, n_vbs - (int32_t)strip * kGroupV);  // last strip may be narrow
+  const int32_t vb = vb_begin + (int32_t)strip * kGroupV + r_in % strip_w;
   const int32_t tb = r_in / strip_w;
   const int32_t v0 = vb * kBV;
   const int32_t t0 = tb * kBT;
@@ -154,13 +163,14 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   // instruction; lane i of instruction j fetches row 32w + 8j + i/8 at the chunk
   // that belongs at LDS position i%8.  Offsets are in 16-byte chunks from the
   // operand base (the boundary checks that both operands hold fewer than 2^31
-  // chunks); padding rows of W and rows past the last token are never read.
+  // chunks); rows of W outside [row_lo, row_hi) -- padding, other shards --
+  // and rows past the last token are never read.
   int32_t woff[kLoads], hoff[kLoads];
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const int row = wave * kRowsPerWave + j * kRowsPerLoad + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    woff[j] = min(v0 + row, real_vocab - 1) * ldc + c;
+    woff[j] = min(max(v0 + row, row_lo), row_hi - 1) * ldc + c;
     hoff[j] = min(t0 + row, num_tokens - 1) * ldc + c;
   }
 
@@ -271,8 +281,9 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   const int32_t vw0 = v0 + wv * 128;            // first vocabulary row of this wave
   const int32_t row_lane = 4 * (lane >> 4);     // lane-group offset inside a 16-row tile
   float* xch = reinterpret_cast<float*>(smem);  // [256 tokens][4]
-  // every row of the block is real and no tile bound cuts it: one segment, no masks
-  const bool simple = (v0 + kBV <= real_vocab) && (bnd == v0 + kBV);
+  // every row of the block is in [row_lo, row_hi) and no tile bound cuts it:
+  // one segment, no masks
+  const bool simple = (v0 >= row_lo) && (v0 + kBV <= row_hi) && (bnd == v0 + kBV);
 
 #pragma unroll
   for (int ts = 0; ts < kTS; ++ts) {
@@ -280,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     int32_t trow = -1;  // the target's column if this wave holds it
     if (tok < num_tokens && (mask == nullptr || mask[tok] != 0)) {
       const int32_t tg = targets[tok];
-      if (tg != ignore_index && tg >= vw0 && tg < vw0 + 128 && tg < real_vocab) trow = tg;
+      if (tg != ignore_index && tg >= vw0 && tg < vw0 + 128 && tg >= row_lo && tg < row_hi)
+        trow = tg;
     }
     if (__any(trow >= 0)) {  // rare: some token of this wave has its target here
       float tz = 0.0f;
@@ -312,15 +324,16 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 #pragma unroll
         for (int i = 0; i < 4; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
     } else {
-      // pass 1: per-segment maxima over this lane's real rows
+      // pass 1: per-segment maxima over this lane's rows in [row_lo, row_hi)
 #pragma unroll
       for (int vs = 0; vs < kVS; ++vs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int32_t row = vw0 + vs * 16 + row_lane + i;
           const float z = acc[vs][ts][i];
-          if (row < real_vocab && row < bnd) m0 = maxnan(m0, z);
-          if (row < real_vocab && row >= bnd) m1 = maxnan(m1, z);
+          const bool in = row >= row_lo && row < row_hi;
+          if (in && row < bnd) m0 = maxnan(m0, z);
+          if (in && row >= bnd) m1 = maxnan(m1, z);
         }
       m0 = maxnan(m0, __shfl_xor(m0, 16));
       m0 = maxnan(m0, __shfl_xor(m0, 32));
@@ -329,8 +342,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
       // pass 2: sums of exp(z - max) relative to the token's maxima.  The two
       // thresholds go through an empty asm so the compiler recomputes the row
       // tests here instead of keeping 128 masks alive from pass 1.
-      int32_t rv = real_vocab, bd = bnd;
-      asm volatile("" : "+s"(rv), "+s"(bd));
+      int32_t lo = row_lo, rv = row_hi, bd = bnd;
+      asm volatile("" : "+s"(lo), "+s"(rv), "+s"(bd));
       const float b0 = (m0 == kNegInf) ? 0.0f : m0;
       const float b1 = (m1 == kNegInf) ? 0.0f : m1;
 #pragma unroll
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int32_t row = vw0 + vs * 16 + row_lane + i;
-          const float z = (row < rv) ? acc[vs][ts][i] : kNegInf;
+          const float z = (row >= lo && row < rv) ? acc[vs][ts][i] : kNegInf;
           const bool hi = row >= bd;
           const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
           s0 += hi ? 0.0f : e;
@@ -367,6 +380,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
     }
   }
   __syncthreads();
+  // slot 0 starts at v0; slot 1 at the inner bound, or (an identity slot that
+  // nothing reads) at v0 when there is none
+  const int32_t c_slot1 = (bnd < v0 + kBV) ? bnd : v0;
+  const bool own0 = v0 >= col_lo && v0 < col_hi;
+  const bool own1 = c_slot1 >= col_lo && c_slot1 < col_hi;
   if (wv == 0 && lane < 16) {
     const int64_t seg_ld = 2 * (int64_t)n_vb;
 #pragma unroll
@@ -391,47 +409,57 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
       }
       float* om = seg_m + (int64_t)tok * seg_ld + 2 * vb;
       float* os = seg_s + (int64_t)tok * seg_ld + 2 * vb;
-      om[0] = out_m[0];
-      om[1] = out_m[1];
-      os[0] = out_s[0];
-      os[1] = out_s[1];
+      if (own0) {
+        om[0] = out_m[0];
+        os[0] = out_s[0];
+      }
+      if (own1) {
+        om[1] = out_m[1];
+        os[1] = out_s[1];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// lmhead_tiles: one thread per (token, tile); segments in ascending columns.
+// lmhead_tiles: one thread per (token, tile) of the tiles [tile_begin,
+// tile_begin + n_tiles); segments in ascending columns.  A tile that starts at
+// or past real_vocab has no real column: the identity (-inf, 0), with no read.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lmhead_tiles(
     const float* __restrict__ seg_m, const float* __restrict__ seg_s, int32_t num_tokens,
-    int32_t n_vb, int32_t padded_vocab, int32_t num_tiles, float* __restrict__ pmax,
-    float* __restrict__ psum, int64_t idx_begin) {
+    int32_t n_vb, int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles,
+    int32_t tile_begin, int32_t n_tiles, float* __restrict__ pmax, float* __restrict__ psum,
+    int64_t idx_begin) {
   const int64_t idx = idx_begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)num_tokens * num_tiles) return;
-  const int32_t tok = (int32_t)(idx / num_tiles);
-  const int32_t t = (int32_t)(idx - (int64_t)tok * num_tiles);
+  if (idx >= (int64_t)num_tokens * n_tiles) return;
+  const int32_t tok = (int32_t)(idx / n_tiles);
+  const int32_t t = tile_begin + (int32_t)(idx - (int64_t)tok * n_tiles);
   const int32_t c0 = (int32_t)(((int64_t)t * padded_vocab) / num_tiles);
   const int32_t c1 = (int32_t)(((int64_t)(t + 1) * padded_vocab) / num_tiles);
-  const int32_t vb_first = c0 / kBV;
-  const int32_t vb_last = min((c1 - 1) / kBV, n_vb - 1);
-  const int64_t seg_ld = 2 * (int64_t)n_vb;
+  const int64_t out = (int64_t)tok * num_tiles + t;
   float M = kNegInf, S = 0.0f;
-  for (int32_t vb = vb_first; vb <= vb_last; ++vb) {
-    const int slot = (vb == vb_first && c0 > vb * kBV) ? 1 : 0;
-    const float m = seg_m[(int64_t)tok * seg_ld + 2 * vb + slot];
-    const float s = seg_s[(int64_t)tok * seg_ld + 2 * vb + slot];
-    if (m == kNegInf) continue;  // identity segment
-    if (M == kNegInf) {
-      M = m;
-      S = s;
-      continue;
+  if (c0 < real_vocab) {
+    const int32_t vb_first = c0 / kBV;
+    const int32_t vb_last = min((min(c1, real_vocab) - 1) / kBV, n_vb - 1);
+    const int64_t seg_ld = 2 * (int64_t)n_vb;
+    for (int32_t vb = vb_first; vb <= vb_last; ++vb) {
+      const int slot = (vb == vb_first && c0 > vb * kBV) ? 1 : 0;
+      const float m = seg_m[(int64_t)tok * seg_ld + 2 * vb + slot];
+      const float s = seg_s[(int64_t)tok * seg_ld + 2 * vb + slot];
+      if (m == kNegInf) continue;  // identity segment
+      if (M == kNegInf) {
+        M = m;
+        S = s;
+        continue;
+      }
+      const float nm = maxnan(M, m);
+      S = fmaf(s, exp2_hw((m - nm) * kLog2e), S * exp2_hw((M - nm) * kLog2e));
+      M = nm;
     }
-    const float nm = maxnan(M, m);
-    S = fmaf(s, exp2_hw((m - nm) * kLog2e), S * exp2_hw((M - nm) * kLog2e));
-    M = nm;
   }
-  pmax[idx] = M;
-  psum[idx] = (M == kNegInf) ? 0.0f : S;
+  pmax[out] = M;
+  psum[out] = (M == kNegInf) ? 0.0f : S;
 }
 
 }  // namespace
@@ -447,29 +475,44 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream) {
   const int32_t n_vb = (a.real_vocab + kBV - 1) / kBV;
   const int32_t n_tb = (a.num_tokens + kBT - 1) / kBT;
   const int64_t limit = launch_thread_limit();
-  // the GEMM blocks in launches of at most limit / kThreads blocks; a block's
-  // work index (and so its tile) does not depend on the split
-  const int64_t blocks = (int64_t)n_vb * n_tb;
   const int64_t max_blocks = limit / kThreads;
-  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {
-    const int64_t nb = blocks - b0 < max_blocks ? blocks - b0 : max_blocks;
-    hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)nb), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const u32x4*>(a.hidden),
-                       reinterpret_cast<const u32x4*>(a.weight), a.hidden_dim, a.num_tokens,
-                       a.real_vocab, a.padded_vocab, a.num_tiles, n_vb, n_tb, a.targets, a.mask,
-                       a.ignore_index, a.seg_m, a.seg_s, a.target_logit, b0);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t items = (int64_t)a.num_tokens * a.num_tiles;
   const int64_t max_items = limit / 256 * 256;
-  for (int64_t i0 = 0; i0 < items; i0 += max_items) {
-    const int64_t ni = items - i0 < max_items ? items - i0 : max_items;
-    hipLaunchKernelGGL(lmhead_tiles, dim3((unsigned)((ni + 255) / 256)), dim3(256), 0, stream,
-                       a.seg_m, a.seg_s, a.num_tokens, n_vb, a.padded_vocab, a.num_tiles, a.pmax,
-                       a.psum, i0);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  auto bound = [&](int64_t t) { return (int32_t)((t * a.padded_vocab) / a.num_tiles); };
+  // Virtual shard s owns tiles [floor(s*T/S), floor((s+1)*T/S)): its GEMM
+  // blocks, then its tiles' partials.  A block cut by a shard bound is
+  // computed by both shards, each over its own rows.
+  for (int32_t s = 0; s < a.num_shards; ++s) {
+    const int32_t ta = (int32_t)(((int64_t)s * a.num_tiles) / a.num_shards);
+    const int32_t tb = (int32_t)(((int64_t)(s + 1) * a.num_tiles) / a.num_shards);
+    const int32_t col_lo = bound(ta), col_hi = bound(tb);
+    const int32_t row_hi = col_hi < a.real_vocab ? col_hi : a.real_vocab;
+    if (col_lo < row_hi) {  // a shard of padding only has no GEMM block
+      const int32_t vb_begin = col_lo / kBV;
+      const int32_t n_vbs = (row_hi - 1) / kBV + 1 - vb_begin;
+      // launches of at most limit / kThreads blocks; a block's work index (and
+      // so its tile) does not depend on the split
+      const int64_t blocks = (int64_t)n_vbs * n_tb;
+      for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {
+        const int64_t nb = blocks - b0 < max_blocks ? blocks - b0 : max_blocks;
+        hipLaunchKernelGGL(lmhead_segments, dim3((unsigned)nb), dim3(kThreads), 0, stream,
+                           reinterpret_cast<const u32x4*>(a.hidden),
+                           reinterpret_cast<const u32x4*>(a.weight), a.hidden_dim, a.num_tokens,
+                           a.padded_vocab, a.num_tiles, n_vb, n_tb, vb_begin, n_vbs, col_lo,
+                           row_hi, col_lo, col_hi, a.targets, a.mask, a.ignore_index, a.seg_m,
+                           a.seg_s, a.target_logit, b0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
+    const int64_t items = (int64_t)a.num_tokens * (tb - ta);
+    for (int64_t i0 = 0; i0 < items; i0 += max_items) {
+      const int64_t ni = items - i0 < max_items ? items - i0 : max_items;
+      hipLaunchKernelGGL(lmhead_tiles, dim3((unsigned)((ni + 255) / 256)), dim3(256), 0, stream,
+                         a.seg_m, a.seg_s, a.num_tokens, n_vb, a.real_vocab, a.padded_vocab,
+                         a.num_tiles, ta, tb - ta, a.pmax, a.psum, i0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
