@@ -380,8 +380,9 @@ __device__ __forceinline__ float lse_of(float M, double S) {
 }
 
 // LSE from a row's T partials: exact max first, then the rescaled sum in
-// ascending tile order with fmaf, skipping identity partials; -inf if every
-// partial is the identity.  pm/ps point at the row's T values.
+// ascending tile order (fp32 exponentials, an fp64 fma chain), skipping
+// identity partials, rounded to fp32 once in lse_of; -inf if every partial is
+// the identity.  pm/ps point at the row's T values.
 __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
                                            const float* __restrict__ ps, int32_t num_tiles) {
   if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
@@ -765,7 +766,7 @@ constexpr int kFbUnroll = 4;
 
 // The stage-2 merge of T <= 64 partials held one per lane of a wave (lane t
 // holds tile t; lanes >= T hold the identity).  The max is exact in any order
-// and the exponentials are taken in parallel; the fmaf chain then runs in
+// and the exponentials are taken in parallel; the fma chain then runs in
 // ascending tile order over LDS copies, in fp64 as in merge_row.  An identity
 // partial enters the chain as fma(0, 0, S), which is S (S >= +0), exactly as if
 // it were skipped.  Every lane returns the LSE.
