@@ -121,6 +121,37 @@ LMHEAD_WORKLOAD = "lmhead_b4096_k4096_v151936_p152576"
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, vendor figure
 
 
+def cpu_baseline_lmhead(h, w, tgt, v_real: int, max_seconds: float) -> dict:
+    """The oracle (z = h . W^T in fp64 with plain loops, threads over vocabulary columns,
+    then the fp64 log-softmax) on leading tokens of the LM-head workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    orc = oracle.get()
+    cores = max(1, min(16, os.cpu_count() or 1))
+    n, k = h.shape
+    hb = h.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    wb = w[:v_real].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    tg = tgt.cpu().numpy()
+    block = 4
+    done, elapsed = 0, 0.0
+    while done < n and elapsed < max_seconds:
+        r1 = min(n, done + block)
+        t0 = time.perf_counter()
+        z = orc.lmhead_logits(hb[done:r1], wb, real_vocab=v_real, nthreads=cores)
+        orc.fwd(z, tg[done:r1], None, real_vocab=v_real, nthreads=cores, raise_on_error=False)
+        elapsed += time.perf_counter() - t0
+        done = r1
+    flops = 2.0 * done * v_real * k
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"tokens 0..{done - 1} of the same workload ({done} of {n} tokens): "
+                      f"h . W^T in fp64, then the fp64 log-softmax, {elapsed:.1f} s",
+            "tokens_per_s": round(done / elapsed, 3)}
+
+
 def bench_lmhead(args) -> int:
     """The fused LM-head variant: hidden [4096, 4096] ~ N(0,1), W [152576, 4096] ~ N(0, 0.02^2),
     rows >= 151936 padding, 64 tiles, all tokens active, forward only."""
@@ -168,6 +199,10 @@ def bench_lmhead(args) -> int:
         lib_ms = e0.elapsed_time(e1) / args.steps
         library = {"ms": round(lib_ms, 4), "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
                    "note": "torch.matmul bf16 -> bf16 logits (materialised), no logp"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_lmhead(h, w, tgt, v_real, args.cpu_seconds)
     line = {
         "metric": "fused LM-head selected-token logp, TFLOP/s (MFMA utilisation)",
         "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -181,7 +216,7 @@ def bench_lmhead(args) -> int:
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "lmhead_segments+lmhead_tiles+stage2_merge"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "library_gemm": library,
     }
     print(json.dumps(line), flush=True)

@@ -218,14 +218,14 @@ __device__ __forceinline__ void tile_range(int32_t tile, int32_t tile_width, int
 //      chunks are masked (leading and trailing passes);
 //   3. the 16 lanes combined by an exact max and a fixed rotate tree.
 // kNt selects the nontemporal load hint and kDepth the number of passes whose
-// loads are in flight (1 or 2); neither changes the arithmetic.  With kEnt the
+// loads are in flight (1, 2 or 3); neither changes the arithmetic.  With kEnt the
 // group also returns la = sum exp(x - gm) (x - gm) over the tile (0 for the
 // identity partial); gm and ls are the same bits with or without it.
 template <bool kNt, int kDepth, bool kEnt = false>
 __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int32_t lo,
                                              int32_t hi, int gl, float& gm_out, float& ls_out,
                                              float& la_out) {
-  static_assert(kDepth == 1 || kDepth == 2, "prefetch depth is 1 or 2 passes");
+  static_assert(kDepth >= 1 && kDepth <= 3, "prefetch depth is 1, 2 or 3 passes");
   float m = kNegInf, s = 0.0f, a = 0.0f;
   const int32_t cf_lo = (lo + 7) >> 3;  // first full chunk
   int32_t cf_hi = hi >> 3;              // end of full chunks
@@ -248,11 +248,12 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
   }
   uint4 qe;
   if (c >= 0) qe = load_chunk<kNt>(rowp + c);
-  uint4 qa[kChunks], qb[kChunks];
-  if (kDepth == 2) {
+  uint4 qa[kChunks], qb[kChunks], qc[kChunks];
+  if (kDepth >= 2) {
     if (npass > 0) load_pass<kNt>(qa, rowp, base0, cf_lo, cf_hi, gl);
     if (npass > 1) load_pass<kNt>(qb, rowp, base0 + kPassChunks, cf_lo, cf_hi, gl);
   }
+  if (kDepth == 3 && npass > 2) load_pass<kNt>(qc, rowp, base0 + 2 * kPassChunks, cf_lo, cf_hi, gl);
   if (c >= 0) {
     float v[8];
     unpack8(qe, v);
@@ -266,6 +267,19 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
       const int32_t b = base0 + p * kPassChunks;
       load_pass<kNt>(qa, rowp, b, cf_lo, cf_hi, gl);
       fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
+    }
+  } else if (kDepth == 3) {
+    // three passes in flight: pass p + 3 is issued as soon as pass p has folded
+    for (int32_t p = 0; p < npass; p += 3) {
+      const int32_t b = base0 + p * kPassChunks;
+      fold_pass<kEnt>(qa, b, cf_lo, cf_hi, gl, m, s, a);
+      if (p + 3 < npass) load_pass<kNt>(qa, rowp, b + 3 * kPassChunks, cf_lo, cf_hi, gl);
+      if (p + 1 >= npass) break;
+      fold_pass<kEnt>(qb, b + kPassChunks, cf_lo, cf_hi, gl, m, s, a);
+      if (p + 4 < npass) load_pass<kNt>(qb, rowp, b + 4 * kPassChunks, cf_lo, cf_hi, gl);
+      if (p + 2 >= npass) break;
+      fold_pass<kEnt>(qc, b + 2 * kPassChunks, cf_lo, cf_hi, gl, m, s, a);
+      if (p + 5 < npass) load_pass<kNt>(qc, rowp, b + 5 * kPassChunks, cf_lo, cf_hi, gl);
     }
   } else {
     // two passes in flight: pass p + 2 is issued as soon as pass p has folded
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(kWPB * 64) void stage1_partials(
   const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
 
   float gm, ls, la;
-  tile_partial<true, 2, kEnt>(rowp, lo, hi, gl, gm, ls, la);
+  tile_partial<true, 3, kEnt>(rowp, lo, hi, gl, gm, ls, la);
 
   if (have && gl == 0) {
     const int64_t o = (int64_t)row * num_tiles + tile;
