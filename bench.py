@@ -12,6 +12,11 @@ Prints ONE JSON line on stdout.  Everything else goes to stderr.
                FETCH_SIZE / WRITE_SIZE counters (committed under profiles/),
                reported only while the kernel source is unchanged since then
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows
+  one_read_accounting
+               the same workload counted as one read of every real logit and one
+               write of every dX element per step (what the one-launch schedule
+               moves), with the two calls' rate under that count and the
+               one-launch schedule (rlk_logp_fwd_bwd) timed on the same inputs
 """
 from __future__ import annotations
 
@@ -232,6 +237,8 @@ def main() -> int:
     ap.add_argument("--shards", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alt-schedule", action="store_true",
+                    help="skip timing the one-launch schedule beside the two calls")
     ap.add_argument("--one-pass", action="store_true",
                     help="time rlk_logp_fwd_bwd (g known before the forward) instead of "
                          "rlk_logp_fwd + rlk_logp_bwd")
@@ -345,6 +352,33 @@ def main() -> int:
     log(f"bench: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms; "
         f"step p10/p50/p90 {step_spread['p10']}/{step_spread['p50']}/{step_spread['p90']} ms)")
 
+    # The same workload under the other accounting: one read of every real logit and
+    # one write of every dX element per step, which only the one-launch schedule
+    # (rlk_logp_fwd_bwd, for a g known before the forward) reaches; timed on the
+    # same inputs so that both schedules appear in the one line.
+    one_read = None
+    if wl.backward and not one_pass and not extended and not args.no_alt_schedule:
+        def step_one(i):
+            b, m = inps[i % 2], masks[i % 2]
+            rlk.rlk_logp_fwd_bwd(desc, b.logits, b.targets, m, b.grad, logp, lse, dl, ld_d, code,
+                                 ws, stream)
+        for i in range(args.warmup):
+            step_one(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_one(i)
+        torch.cuda.synchronize()
+        ms_one = (time.perf_counter() - t0) * 1e3 / args.steps
+        b_one = algorithmic_bytes_one_pass(wl)
+        one_read = {"bytes_per_step": b_one,
+                    "two_calls_GB/s": round(b_one / (ms_step * 1e-3) / 1e9, 1),
+                    "one_launch_ms_per_step": round(ms_one, 4),
+                    "one_launch_GB/s": round(b_one / (ms_one * 1e-3) / 1e9, 1),
+                    "one_launch_hbm_frac": round(b_one / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "one_launch_tokens_per_s": round(n / (ms_one * 1e-3), 1)}
+        log(f"bench: one-launch schedule {ms_one:.3f} ms/step")
+
     if args.copy_probe_gib > 0:  # plain copy kernel of known size, for counter scaling
         nbytes = int(args.copy_probe_gib * 2 ** 30)
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -413,6 +447,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if one_read is not None:
+        line["one_read_accounting"] = one_read
     print(json.dumps(line), flush=True)
     return 0
 
