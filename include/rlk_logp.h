@@ -58,6 +58,11 @@
  *     reports them as RLK_ERR_TARGET_RANGE / RLK_ERR_NONFINITE_LSE.
  *   - There is one code path and no fallback: if the GPU path cannot run, the
  *     call fails.
+ *   - Graph capture: without RLK_FLAG_VALIDATE a call enqueues kernel launches
+ *     only -- no allocation, memset, copy or synchronisation -- so it may be
+ *     captured into a HIP graph and replayed; the replays read whatever the
+ *     captured buffers hold at the time.  With the flag the call synchronises
+ *     and copies the status words to the host, so it cannot be captured.
  *   - Batch size: a dispatch holds its grid size in 32 bits of threads, so a
  *     large batch is split into several launches of at most 2^31 threads each
  *     (the backward of 152576-column rows, at 75 blocks of 128 threads per
