@@ -173,11 +173,13 @@ def test_fused_repeat_and_batch_invariance():
 def test_fused_validate_bad_target():
     h, w, tgt, mask = make_case(40, 64, 1000, 1024, seed=5, mask_keep=1.1, ignore_frac=0.0)
     tgt[7] = 1000  # a padded column is not a valid target
-    with pytest.raises(rlk.RlkError) as ei:
-        run(h, w, tgt, None, 1000, 1024, 4, validate=True)
-    assert ei.value.status == rlk.RLK_ERR_TARGET_RANGE
-    logp, _, _ = run(h, w, tgt, None, 1000, 1024, 4)
-    assert torch.isnan(logp[7]) and torch.isfinite(logp[torch.arange(40, device=DEV) != 7]).all()
+    for shards in (1, 2, 4):
+        with pytest.raises(rlk.RlkError) as ei:
+            run(h, w, tgt, None, 1000, 1024, 4, validate=True, shards=shards)
+        assert ei.value.status == rlk.RLK_ERR_TARGET_RANGE
+        logp, _, _ = run(h, w, tgt, None, 1000, 1024, 4, shards=shards)
+        assert torch.isnan(logp[7])
+        assert torch.isfinite(logp[torch.arange(40, device=DEV) != 7]).all()
 
 
 def test_fused_lmhead_4096_sampled():
