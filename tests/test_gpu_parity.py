@@ -347,3 +347,29 @@ def test_small_and_large_launch_shapes_agree():
     _, _, e_one = rlk.forward_ex(inp.logits[7:8], inp.targets[7:8], inp.mask[7:8],
                                  real_vocab=wl.real_vocab)
     assert torch.equal(e_one.view(torch.int32), e_big[7:8].view(torch.int32))
+
+
+@pytest.mark.parametrize("tiles", [64, 16])
+def test_batch_invariance_across_stage2_forms(tiles):
+    """Batches of up to 4096 rows merge with one wave per row, larger ones with one
+    thread per row; a row gives the same bits either way, including rows whose
+    logits are all -inf, hold a NaN or hold +inf."""
+    wl = W.small_workload(5000, 5000, 5120, num_tiles=tiles, sigma=3.0, mask_keep=0.9,
+                          ignore_frac=0.05, seed=4096 + tiles)
+    inp = W.make_inputs(wl, DEV)
+    x = inp.logits
+    x[3, :wl.real_vocab] = float("-inf")
+    x[10, 77] = float("nan")
+    x[20, 4000] = float("inf")
+    x[21, :wl.real_vocab] = float("-inf")
+    x[21, 123] = 2.5  # one finite value: LSE is exactly that value
+    big = fwd(inp)
+    rows = torch.tensor(sorted({3, 10, 20, 21} | set(range(0, 5000, 79))), device=DEV)
+    assert len(rows) <= 4096
+    sub = W.Inputs(wl, x[rows].contiguous(), inp.targets[rows], inp.mask[rows], inp.grad[rows])
+    small = fwd(sub)
+    assert torch.equal(small[0].view(torch.int32), big[0][rows].view(torch.int32))
+    assert torch.equal(small[1].view(torch.int32), big[1][rows].view(torch.int32))
+    lse = big[1].cpu()
+    assert lse[3] == float("-inf") and torch.isnan(lse[10]) and lse[21] == 2.5
+    assert torch.isnan(lse[20]) or lse[20] == float("inf")
