@@ -373,3 +373,11 @@ def test_batch_invariance_across_stage2_forms(tiles):
     lse = big[1].cpu()
     assert lse[3] == float("-inf") and torch.isnan(lse[10]) and lse[21] == 2.5
     assert torch.isnan(lse[20]) or lse[20] == float("inf")
+    # the same with the entropy output (its own wave-per-row merge)
+    kw = dict(real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab, num_vocab_tiles=tiles)
+    big_ex = rlk.forward_ex(x, inp.targets, inp.mask, **kw)
+    small_ex = rlk.forward_ex(sub.logits, sub.targets, sub.mask, **kw)
+    for a, b in zip(small_ex, big_ex):
+        assert torch.equal(a.view(torch.int32), b[rows].view(torch.int32))
+    assert torch.equal(big_ex[1].view(torch.int32), big[1].view(torch.int32))
+    assert float(big_ex[2][21]) == 0.0  # one finite value: no uncertainty

@@ -809,11 +809,54 @@ __device__ __forceinline__ float merge_lanes(float mt, float st, int32_t num_til
   return lse_of(M, S);
 }
 
+// merge_row_entropy with the T <= 64 partials held one per lane: the max and the
+// exponentials as in merge_lanes, then the fp64 chains for S and A in ascending
+// tile order over LDS copies.  An identity lane enters both chains as
+// fma(0, 0, .), which leaves S (>= +0) and A (+0 or negative) unchanged, exactly
+// as if it were skipped.  Every lane returns the LSE and H.
+__device__ __forceinline__ float merge_lanes_entropy(float mt, float st, float at,
+                                                     int32_t num_tiles, int lane, float* s_e,
+                                                     float* s_sv, float* s_d, float* s_a,
+                                                     float& H) {
+  H = __builtin_nanf("");
+  float M = mt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = maxnan(M, __shfl_xor(M, o));
+  if (M == kNegInf) return kNegInf;
+  const bool live = lane < num_tiles && mt != kNegInf;
+  const float d = live ? mt - M : 0.0f;
+  s_e[lane] = live ? expf(d) : 0.0f;
+  s_sv[lane] = live ? st : 0.0f;
+  s_d[lane] = d;
+  s_a[lane] = live ? at : 0.0f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double S = 0.0, A = 0.0;
+#pragma unroll
+  for (int t = 0; t < 64; t += 4) {
+    const float4 e4 = *reinterpret_cast<const float4*>(s_e + t);
+    const float4 s4 = *reinterpret_cast<const float4*>(s_sv + t);
+    const float4 d4 = *reinterpret_cast<const float4*>(s_d + t);
+    const float4 a4 = *reinterpret_cast<const float4*>(s_a + t);
+    const float ev[4] = {e4.x, e4.y, e4.z, e4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float dv[4] = {d4.x, d4.y, d4.z, d4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      S = fma((double)sv[j], (double)ev[j], S);
+      A = fma((double)ev[j], fma((double)dv[j], (double)sv[j], (double)av[j]), A);
+    }
+  }
+  const float L = lse_of(M, S);
+  if (__builtin_isfinite(L)) H = (float)(log(S) - A / S);
+  return L;
+}
+
 // ---------------------------------------------------------------------------
 // Stage 2 with one wave per row, for T <= 64: lane t holds tile t's partial and
-// merge_lanes takes the exponentials in parallel, so a row costs one exp per
-// lane instead of T in one thread; the arithmetic, and so every output bit, is
-// that of stage2_merge.  Rows [row_begin, row_begin + gridDim.x * kMergeRows)
+// merge_lanes (merge_lanes_entropy with the entropy output) takes the
+// exponentials in parallel, so a row costs one exp per lane instead of T in one
+// thread; the arithmetic, and so every output bit, is that of stage2_merge.  Rows [row_begin, row_begin + gridDim.x * kMergeRows)
 // of the batch; a wave past num_rows returns at once.
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 4;  // rows (waves) per block
@@ -823,14 +866,22 @@ constexpr int kMergeRows = 4;  // rows (waves) per block
 // us, 8192 rows level, 16384 rows 741 against 735 us (each wave's serial fp64
 // chain then costs more than the exponentials it spreads over lanes).
 constexpr int64_t kMergeWaveMaxRows = 4096;
+// With the entropy output a wave runs two fp64 chains, so the crossover comes
+// earlier: forward_ex times 11.4 against 16.1 us at 32 rows, 62.4 against 66.5 us
+// at 1024 rows, 219.9 against 215.1 us at 4096 rows.
+constexpr int64_t kMergeWaveMaxRowsEnt = 2048;
+template <bool kEnt>
 __global__ __launch_bounds__(kMergeRows * 64) void stage2_merge_waves(
     const uint16_t* __restrict__ logits, const float* __restrict__ target_logit, int64_t ld,
     int32_t num_rows, int32_t real_vocab, int32_t num_tiles, const float* __restrict__ pmax,
-    const float* __restrict__ psum, const int32_t* __restrict__ targets,
-    const uint8_t* __restrict__ mask, int32_t ignore_index, float* __restrict__ logp,
-    float* __restrict__ lse, uint32_t* __restrict__ status, int64_t row_begin) {
+    const float* __restrict__ psum, const float* __restrict__ pent,
+    const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
+    float* __restrict__ logp, float* __restrict__ lse, float* __restrict__ entropy,
+    uint32_t* __restrict__ status, int64_t row_begin) {
   __shared__ __align__(16) float s_e[kMergeRows][64];
   __shared__ __align__(16) float s_sv[kMergeRows][64];
+  __shared__ __align__(16) float s_d[kEnt ? kMergeRows : 1][64];
+  __shared__ __align__(16) float s_a[kEnt ? kMergeRows : 1][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t r = row_begin + (int64_t)blockIdx.x * kMergeRows + w;
@@ -846,9 +897,16 @@ __global__ __launch_bounds__(kMergeRows * 64) void stage2_merge_waves(
                      : __uint_as_float((uint32_t)logits[r * ld + tgt] << 16);
   const float mt = lane < num_tiles ? pmax[r * num_tiles + lane] : kNegInf;
   const float st = lane < num_tiles ? psum[r * num_tiles + lane] : 0.0f;
-  const float L = merge_lanes(mt, st, num_tiles, lane, s_e[w], s_sv[w]);
+  float L, H = 0.0f;
+  if constexpr (kEnt) {
+    const float at = lane < num_tiles ? pent[r * num_tiles + lane] : 0.0f;
+    L = merge_lanes_entropy(mt, st, at, num_tiles, lane, s_e[w], s_sv[w], s_d[w], s_a[w], H);
+  } else {
+    L = merge_lanes(mt, st, num_tiles, lane, s_e[w], s_sv[w]);
+  }
   if (lane == 0) {
     lse[r] = L;
+    if (kEnt) entropy[r] = H;
     if (!act) {
       logp[r] = 0.0f;
     } else if (bad) {
@@ -1057,16 +1115,25 @@ hipError_t launch_stage1(const Stage1Args& a, hipStream_t stream) {
 
 hipError_t launch_stage2(const Stage2Args& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
-  if (!a.entropy && a.num_tiles <= 64 && a.num_rows <= kMergeWaveMaxRows) {
+  if (a.num_tiles <= 64 &&
+      a.num_rows <= (a.entropy ? kMergeWaveMaxRowsEnt : kMergeWaveMaxRows)) {
     // one wave per row, in launches of at most launch_thread_limit() threads
     const int64_t rows_per_launch = launch_thread_limit() / 64 / kMergeRows * kMergeRows;
     for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
       const int64_t nr = a.num_rows - r0 < rows_per_launch ? a.num_rows - r0 : rows_per_launch;
-      hipLaunchKernelGGL(stage2_merge_waves, dim3((unsigned)((nr + kMergeRows - 1) / kMergeRows)),
-                         dim3(kMergeRows * 64), 0, stream,
-                         reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
-                         a.num_rows, a.real_vocab, a.num_tiles, a.pmax, a.psum, a.targets,
-                         a.mask, a.ignore_index, a.logp, a.lse, a.status, r0);
+      const dim3 grid((unsigned)((nr + kMergeRows - 1) / kMergeRows));
+      if (a.entropy)
+        hipLaunchKernelGGL(stage2_merge_waves<true>, grid, dim3(kMergeRows * 64), 0, stream,
+                           reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
+                           a.num_rows, a.real_vocab, a.num_tiles, a.pmax, a.psum, a.pent,
+                           a.targets, a.mask, a.ignore_index, a.logp, a.lse, a.entropy,
+                           a.status, r0);
+      else
+        hipLaunchKernelGGL(stage2_merge_waves<false>, grid, dim3(kMergeRows * 64), 0, stream,
+                           reinterpret_cast<const uint16_t*>(a.logits), a.target_logit, a.ld,
+                           a.num_rows, a.real_vocab, a.num_tiles, a.pmax, a.psum, nullptr,
+                           a.targets, a.mask, a.ignore_index, a.logp, a.lse, nullptr, a.status,
+                           r0);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
