@@ -439,24 +439,40 @@ __global__ __launch_bounds__(256) void lmhead_tiles(
   const int32_t c1 = (int32_t)(((int64_t)(t + 1) * padded_vocab) / num_tiles);
   const int64_t out = (int64_t)tok * num_tiles + t;
   float M = kNegInf, S = 0.0f;
+  // fold one segment into (M, S): identity segments are skipped
+  auto fold = [&](float m, float s) __attribute__((always_inline)) {
+    if (m == kNegInf) return;
+    if (M == kNegInf) {
+      M = m;
+      S = s;
+      return;
+    }
+    const float nm = maxnan(M, m);
+    S = fmaf(s, exp2_hw((m - nm) * kLog2e), S * exp2_hw((M - nm) * kLog2e));
+    M = nm;
+  };
   if (c0 < real_vocab) {
     const int32_t vb_first = c0 / kBV;
     const int32_t vb_last = min((min(c1, real_vocab) - 1) / kBV, n_vb - 1);
-    const int64_t seg_ld = 2 * (int64_t)n_vb;
-    for (int32_t vb = vb_first; vb <= vb_last; ++vb) {
-      const int slot = (vb == vb_first && c0 > vb * kBV) ? 1 : 0;
-      const float m = seg_m[(int64_t)tok * seg_ld + 2 * vb + slot];
-      const float s = seg_s[(int64_t)tok * seg_ld + 2 * vb + slot];
-      if (m == kNegInf) continue;  // identity segment
-      if (M == kNegInf) {
-        M = m;
-        S = s;
-        continue;
+    const int32_t nseg = vb_last - vb_first + 1;
+    const int64_t base = (int64_t)tok * 2 * n_vb + 2 * (int64_t)vb_first;
+    const int first_slot = (c0 > vb_first * kBV) ? 1 : 0;  // the tile starts inside its first block
+    // the first kPre segments' loads all go out before the first fold; the
+    // folds then run in ascending column order as before
+    constexpr int kPre = 12;
+    float pm[kPre], ps[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      if (i < nseg) {
+        const int64_t at = base + 2 * i + (i == 0 ? first_slot : 0);
+        pm[i] = seg_m[at];
+        ps[i] = seg_s[at];
       }
-      const float nm = maxnan(M, m);
-      S = fmaf(s, exp2_hw((m - nm) * kLog2e), S * exp2_hw((M - nm) * kLog2e));
-      M = nm;
     }
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      if (i < nseg) fold(pm[i], ps[i]);
+    for (int32_t i = kPre; i < nseg; ++i) fold(seg_m[base + 2 * i], seg_s[base + 2 * i]);
   }
   pmax[out] = M;
   psum[out] = (M == kNegInf) ? 0.0f : S;
