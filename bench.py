@@ -89,9 +89,12 @@ def read_traffic(kernel: str):
     return float(vals[key]) if key in vals else None
 
 
-def cpu_baseline(inp, wl, max_seconds: float) -> dict:
-    """The oracle (fp64 C, one thread per core) on leading rows of the same workload."""
+def cpu_baseline(inp, wl, max_seconds: float, extended=None) -> dict:
+    """The oracle (fp64 C, one thread per core) on leading rows of the same workload.
+    extended = (g_lse, g_ent) device tensors: time the extended forward (entropy) and
+    backward (LSE and entropy gradients) the GPU line runs instead of the plain pair."""
     import numpy as np
+    import torch
 
     import oracle
     import workloads as W
@@ -104,21 +107,36 @@ def cpu_baseline(inp, wl, max_seconds: float) -> dict:
         rows = np.arange(done_rows, min(wl.num_tokens, done_rows + block))
         bits, tgt, mask, g = W.to_host(inp, rows)
         act = mask & (tgt != W.IGNORE_INDEX)
+        if extended is not None:
+            sel = torch.as_tensor(rows, device=extended[0].device)
+            gl = extended[0][sel].double().cpu().numpy()
+            gh = extended[1][sel].double().cpu().numpy()
         t0 = time.perf_counter()
         _, lse, _, _ = orc.fwd(bits, tgt, mask, real_vocab=wl.real_vocab, nthreads=cores,
                                raise_on_error=False)
-        orc.bwd(bits, tgt, mask, lse, g, real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
-                nthreads=cores, raise_on_error=False)
+        if extended is None:
+            orc.bwd(bits, tgt, mask, lse, g, real_vocab=wl.real_vocab,
+                    padded_vocab=wl.padded_vocab, nthreads=cores, raise_on_error=False)
+        else:
+            ent = orc.entropy(bits, real_vocab=wl.real_vocab, nthreads=cores)
+            orc.bwd_ex(bits, tgt, mask, lse, real_vocab=wl.real_vocab,
+                       padded_vocab=wl.padded_vocab, ent=ent, g=g, g_lse=gl, g_ent=gh,
+                       nthreads=cores, raise_on_error=False)
         elapsed += time.perf_counter() - t0
         sub = W.Workload(wl.name, 1, len(rows), wl.real_vocab, wl.padded_vocab, wl.sigma,
                          dlogits_dtype=wl.dlogits_dtype)
         b = algorithmic_bytes(sub, int(act.sum()))
         bytes_done += b["fwd"] + b["bwd"]
+        if extended is not None:  # as the GPU line counts it: every row read again
+            bytes_done += 4 * len(rows) + (len(rows) - int(act.sum())) * wl.real_vocab * 2 \
+                + 12 * len(rows)
         done_rows += len(rows)
+    what = ("fwd with entropy + bwd with LSE and entropy gradients" if extended is not None
+            else "fwd+bwd")
     return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"rows 0..{done_rows - 1} of the same workload ({done_rows} of "
-                      f"{wl.num_tokens} rows), fwd+bwd in fp64, {elapsed:.1f} s",
+                      f"{wl.num_tokens} rows), {what} in fp64, {elapsed:.1f} s",
             "tokens_per_s": round(done_rows / elapsed, 2)}
 
 
@@ -425,7 +443,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds,
+                           extended=(g_lse, g_ent) if extended else None)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
