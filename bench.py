@@ -89,10 +89,11 @@ def read_traffic(kernel: str):
     return float(vals[key]) if key in vals else None
 
 
-def cpu_baseline(inp, wl, max_seconds: float, extended=None) -> dict:
+def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False) -> dict:
     """The oracle (fp64 C, one thread per core) on leading rows of the same workload.
     extended = (g_lse, g_ent) device tensors: time the extended forward (entropy) and
-    backward (LSE and entropy gradients) the GPU line runs instead of the plain pair."""
+    backward (LSE and entropy gradients) the GPU line runs instead of the plain pair.
+    one_pass: count bytes as the one-launch line does (one read, one write)."""
     import numpy as np
     import torch
 
@@ -126,7 +127,7 @@ def cpu_baseline(inp, wl, max_seconds: float, extended=None) -> dict:
         sub = W.Workload(wl.name, 1, len(rows), wl.real_vocab, wl.padded_vocab, wl.sigma,
                          dlogits_dtype=wl.dlogits_dtype)
         b = algorithmic_bytes(sub, int(act.sum()))
-        bytes_done += b["fwd"] + b["bwd"]
+        bytes_done += algorithmic_bytes_one_pass(sub) if one_pass else b["fwd"] + b["bwd"]
         if extended is not None:  # as the GPU line counts it: every row read again
             bytes_done += 4 * len(rows) + (len(rows) - int(act.sum())) * wl.real_vocab * 2 \
                 + 12 * len(rows)
@@ -444,7 +445,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(inp, wl, args.cpu_seconds,
-                           extended=(g_lse, g_ent) if extended else None)
+                           extended=(g_lse, g_ent) if extended else None, one_pass=one_pass)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
