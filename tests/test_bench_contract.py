@@ -1,0 +1,46 @@
+"""The benchmark's contract on the CPU: the one-GPU guard, and the byte counts its
+rates are computed from, against sums written out by hand for the 32768-row
+workload (32768 x 152576 columns, 151936 real, bf16 dX)."""
+from __future__ import annotations
+
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+import workloads as W
+
+ROOT = Path(__file__).resolve().parent.parent
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert r.stdout == ""  # no JSON line
+    assert "one GPU" in r.stderr
+
+
+def test_byte_counts_of_the_large_workload():
+    wl = W.LARGE_32K
+    n, real, pad = 32768, 151936, 152576
+    assert (wl.num_tokens, wl.real_vocab, wl.padded_vocab, wl.dlogits_dtype) == \
+        (n, real, pad, "bf16")
+    active = 27193
+    b = bench.algorithmic_bytes(wl, active)
+    # forward: each real logit once (bf16), and per row target 4 + mask 1 + logp 4 + LSE 4
+    assert b["fwd"] == n * real * 2 + n * (4 + 1 + 4 + 4) == 9_957_703_680
+    # backward: the active rows' real logits, every bf16 dX element, and per row
+    # target 4 + mask 1 + LSE 4 + g 4
+    assert b["bwd"] == active * real * 2 + n * pad * 2 + n * 13
+    # one launch: each real logit read once, each dX element written once, and per
+    # row target 4 + mask 1 + g 4 + logp 4 + LSE 4
+    assert bench.algorithmic_bytes_one_pass(wl) == n * real * 2 + n * pad * 2 + 17 * n \
+        == 19_957_055_488
+
+
+def test_fp32_dlogits_count_four_bytes():
+    wl = W.MICROBATCH_1024
+    assert wl.dlogits_dtype == "f32"
+    b = bench.algorithmic_bytes(wl, 0)
+    assert b["bwd"] == wl.num_tokens * wl.padded_vocab * 4 + 13 * wl.num_tokens
