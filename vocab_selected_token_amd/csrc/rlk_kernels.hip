@@ -856,8 +856,9 @@ __device__ __forceinline__ float merge_lanes_entropy(float mt, float st, float a
 // Stage 2 with one wave per row, for T <= 64: lane t holds tile t's partial and
 // merge_lanes (merge_lanes_entropy with the entropy output) takes the
 // exponentials in parallel, so a row costs one exp per lane instead of T in one
-// thread; the arithmetic, and so every output bit, is that of stage2_merge.  Rows [row_begin, row_begin + gridDim.x * kMergeRows)
-// of the batch; a wave past num_rows returns at once.
+// thread; the arithmetic, and so every output bit, is that of stage2_merge.
+// Rows [row_begin, row_begin + gridDim.x * kMergeRows) of the batch; a wave past
+// num_rows returns at once.
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 4;  // rows (waves) per block
 // Batches up to this many rows take stage2_merge_waves.  Measured against one
