@@ -12,6 +12,11 @@ Prints ONE JSON line on stdout.  Everything else goes to stderr.
                FETCH_SIZE / WRITE_SIZE counters (committed under profiles/),
                reported only while the kernel source is unchanged since then
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows
+  measured_ceilings
+               read-only, write-only and copy stream rates of this GPU from the
+               rlk_calib probe (run first, as a child process); roofline then also
+               carries frac_of_measured: the time the dominant kernel's reads and
+               writes need at those rates, over its measured time
   one_read_accounting
                the same workload counted as one read of every real logit and one
                write of every dX element per step (what the one-launch schedule
@@ -71,6 +76,30 @@ def kernel_source_sha() -> str:
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
+CALIB = Path(__file__).resolve().parent / "vocab_selected_token_amd" / "rlk_calib"
+
+
+def measured_ceilings():
+    """Stream ceilings of this GPU from the rlk_calib probe (8 GiB read-only,
+    write-only and copy streams, 16-byte nontemporal accesses, median of 7), run as
+    a child process before this one touches the GPU; None if it is not built or
+    fails."""
+    import subprocess
+
+    if not CALIB.exists():
+        return None
+    try:
+        r = subprocess.run([str(CALIB)], capture_output=True, text=True, timeout=120)
+        if r.returncode != 0:
+            return None
+        out = json.loads(r.stdout.strip().splitlines()[-1])
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
+    out["source"] = ("rlk_calib: 8 GiB streams, 16-byte nontemporal loads/stores, "
+                     "1 KB per wave instruction, median of 7")
+    return out
 
 
 def read_traffic(kernel: str):
@@ -266,6 +295,8 @@ def main() -> int:
                          "and entropy gradients) instead of rlk_logp_fwd + rlk_logp_bwd")
     ap.add_argument("--library-gemm", action="store_true",
                     help="LM-head workload: also time the library GEMM of the same shape")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the stream-ceiling probe reported beside the roofline")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run an untimed plain copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +304,11 @@ def main() -> int:
         print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-device by design", file=sys.stderr)
         return 2
+
+    ceilings = None
+    if not args.no_ceilings and args.workload != LMHEAD_WORKLOAD:
+        log("bench: measuring stream ceilings (rlk_calib)")
+        ceilings = measured_ceilings()
 
     if args.workload == LMHEAD_WORKLOAD:
         return bench_lmhead(args)
@@ -441,6 +477,20 @@ def main() -> int:
                         "bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
                     "kernel": dom}
 
+    # the dominant kernel against this GPU's measured stream ceilings: the time its
+    # reads need at the read-only rate plus the time its dX writes need at the
+    # write-only rate, over its measured time
+    if ceilings is not None:
+        out_b = 2 if wl.dlogits_dtype == "bf16" else 4
+        k_ms = fwd_ms if (one_pass or roofline["kernel"] != "bwd_dlogits") else bwd_ms
+        k_bytes = kernels[roofline["kernel"]]["bytes"]
+        k_write = n * wl.padded_vocab * out_b if (one_pass or wl.backward and
+                                                  roofline["kernel"] == "bwd_dlogits") else 0
+        bound_ms = ((k_bytes - k_write) / (ceilings["read_GBps"] * 1e9)
+                    + k_write / (ceilings["write_GBps"] * 1e9)) * 1e3
+        roofline["frac_of_measured"] = round(bound_ms / k_ms, 4)
+        roofline["measured_bound_ms"] = round(bound_ms, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
@@ -469,6 +519,7 @@ def main() -> int:
     }
     if one_read is not None:
         line["one_read_accounting"] = one_read
+    line["measured_ceilings"] = ceilings
     print(json.dumps(line), flush=True)
     return 0
 
