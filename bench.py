@@ -118,11 +118,34 @@ def read_traffic(kernel: str):
     return float(vals[key]) if key in vals else None
 
 
-def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False) -> dict:
-    """The oracle (fp64 C, one thread per core) on leading rows of the same workload.
-    extended = (g_lse, g_ent) device tensors: time the extended forward (entropy) and
-    backward (LSE and entropy gradients) the GPU line runs instead of the plain pair.
-    one_pass: count bytes as the one-launch line does (one read, one write)."""
+def host_cpu() -> dict:
+    """The host the oracle runs on: the cores this process may use (its affinity
+    mask), the OMP_NUM_THREADS share a shared machine grants one job, the logical
+    CPU count, and the model name from /proc/cpuinfo."""
+    nproc = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(nproc, int(omp)) if omp.isdigit() and int(omp) > 0 else nproc
+    model = "unknown"
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"threads": max(1, threads), "nproc": nproc, "cpu_count": os.cpu_count(),
+            "omp_num_threads": omp or None, "cpu_model": model}
+
+
+def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False,
+                 single_thread_seconds: float = 4.0) -> dict:
+    """The oracle (fp64 C, threads over rows) on leading rows of the same workload,
+    forward and backward timed separately, on every core the process may use (capped
+    by OMP_NUM_THREADS where the machine sets it), plus a single-thread run over the
+    first rows.  extended = (g_lse, g_ent) device tensors: time the extended forward
+    (entropy) and backward (LSE and entropy gradients) the GPU line runs instead of
+    the plain pair.  one_pass: count bytes as the one-launch line does (one read, one
+    write)."""
     import numpy as np
     import torch
 
@@ -130,11 +153,12 @@ def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False) -> 
     import workloads as W
 
     orc = oracle.get()
-    cores = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    cores = host["threads"]
     block = 256
-    done_rows, elapsed, bytes_done = 0, 0.0, 0.0
-    while done_rows < wl.num_tokens and elapsed < max_seconds:
-        rows = np.arange(done_rows, min(wl.num_tokens, done_rows + block))
+
+    def run(rows, nthreads):
+        """(fwd seconds, bwd seconds, fwd bytes, bwd bytes) over one block of rows."""
         bits, tgt, mask, g = W.to_host(inp, rows)
         act = mask & (tgt != W.IGNORE_INDEX)
         if extended is not None:
@@ -142,32 +166,98 @@ def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False) -> 
             gl = extended[0][sel].double().cpu().numpy()
             gh = extended[1][sel].double().cpu().numpy()
         t0 = time.perf_counter()
-        _, lse, _, _ = orc.fwd(bits, tgt, mask, real_vocab=wl.real_vocab, nthreads=cores,
+        _, lse, _, _ = orc.fwd(bits, tgt, mask, real_vocab=wl.real_vocab, nthreads=nthreads,
                                raise_on_error=False)
+        ent = None
+        if extended is not None:
+            ent = orc.entropy(bits, real_vocab=wl.real_vocab, nthreads=nthreads)
+        t1 = time.perf_counter()
         if extended is None:
             orc.bwd(bits, tgt, mask, lse, g, real_vocab=wl.real_vocab,
-                    padded_vocab=wl.padded_vocab, nthreads=cores, raise_on_error=False)
+                    padded_vocab=wl.padded_vocab, nthreads=nthreads, raise_on_error=False)
         else:
-            ent = orc.entropy(bits, real_vocab=wl.real_vocab, nthreads=cores)
             orc.bwd_ex(bits, tgt, mask, lse, real_vocab=wl.real_vocab,
                        padded_vocab=wl.padded_vocab, ent=ent, g=g, g_lse=gl, g_ent=gh,
-                       nthreads=cores, raise_on_error=False)
-        elapsed += time.perf_counter() - t0
+                       nthreads=nthreads, raise_on_error=False)
+        t2 = time.perf_counter()
         sub = W.Workload(wl.name, 1, len(rows), wl.real_vocab, wl.padded_vocab, wl.sigma,
                          dlogits_dtype=wl.dlogits_dtype)
         b = algorithmic_bytes(sub, int(act.sum()))
-        bytes_done += algorithmic_bytes_one_pass(sub) if one_pass else b["fwd"] + b["bwd"]
+        fb, bb = b["fwd"], b["bwd"]
+        if one_pass:  # one read of each logit for the whole step: charge it to the forward
+            bb = algorithmic_bytes_one_pass(sub) - fb
         if extended is not None:  # as the GPU line counts it: every row read again
-            bytes_done += 4 * len(rows) + (len(rows) - int(act.sum())) * wl.real_vocab * 2 \
-                + 12 * len(rows)
-        done_rows += len(rows)
+            fb += 4 * len(rows)
+            bb += (len(rows) - int(act.sum())) * wl.real_vocab * 2 + 12 * len(rows)
+        return t1 - t0, t2 - t1, fb, bb
+
+    def sweep(nthreads, seconds):
+        done, tf, tb, bf, bb = 0, 0.0, 0.0, 0, 0
+        while done < wl.num_tokens and tf + tb < seconds:
+            rows = np.arange(done, min(wl.num_tokens, done + block))
+            a, b, c, d = run(rows, nthreads)
+            tf, tb, bf, bb = tf + a, tb + b, bf + c, bb + d
+            done += len(rows)
+        return done, tf, tb, bf, bb
+
+    done, tf, tb, bf, bb = sweep(cores, max_seconds)
+    done1, tf1, tb1, bf1, bb1 = sweep(1, single_thread_seconds)
     what = ("fwd with entropy + bwd with LSE and entropy gradients" if extended is not None
             else "fwd+bwd")
-    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"rows 0..{done_rows - 1} of the same workload ({done_rows} of "
-                      f"{wl.num_tokens} rows), {what} in fp64, {elapsed:.1f} s",
-            "tokens_per_s": round(done_rows / elapsed, 2)}
+    rate = lambda nbytes, sec: round(nbytes / sec / 1e9, 4)
+    return {"value": rate(bf + bb, tf + tb), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{done - 1} of the same workload ({done} of {wl.num_tokens} "
+                      f"rows), {what} in fp64 on {cores} threads, {tf + tb:.1f} s; the single-"
+                      f"thread run took rows 0..{done1 - 1}",
+            "tokens_per_s": round(done / (tf + tb), 2),
+            "fwd": {"GB/s": rate(bf, tf), "tokens_per_s": round(done / tf, 2),
+                    "seconds": round(tf, 3)},
+            "bwd": {"GB/s": rate(bb, tb), "tokens_per_s": round(done / tb, 2),
+                    "seconds": round(tb, 3)},
+            "single_thread": {"GB/s": rate(bf1 + bb1, tf1 + tb1), "rows": done1,
+                              "fwd_GB/s": rate(bf1, tf1), "bwd_GB/s": rate(bb1, tb1),
+                              "tokens_per_s": round(done1 / (tf1 + tb1), 2)},
+            "host": host}
+
+
+def sha256_device(t, chunk_bytes: int = 1 << 28) -> str:
+    """SHA-256 of a device tensor's bytes, copied to the host in chunks."""
+    import torch
+
+    flat = t.detach().contiguous().view(-1).view(torch.uint8)
+    h = hashlib.sha256()
+    for o in range(0, flat.numel(), chunk_bytes):
+        h.update(flat[o:o + chunk_bytes].cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def fingerprints(rlk, wl, inp, mask_u8, shard_counts=(1, 8)) -> dict:
+    """SHA-256 of one batch's inputs, and of the fp32 logp and LSE the forward gives
+    for it at each virtual-shard count (the cross-grouping bitwise check): the digests
+    must agree for every count."""
+    import torch
+
+    import workloads as W
+
+    n = wl.num_tokens
+    dev = inp.logits.device
+    out = {"inputs": {"logits": sha256_device(inp.logits), "targets": sha256_device(inp.targets),
+                      "mask": sha256_device(mask_u8), "grad": sha256_device(inp.grad)}}
+    per = {}
+    for s in shard_counts:
+        desc = rlk.make_desc(n, wl.real_vocab, wl.padded_vocab, wl.ld_logits, wl.num_tiles, s,
+                             W.IGNORE_INDEX)
+        ws = rlk.workspace_for(desc, dev)
+        logp = torch.empty(n, dtype=torch.float32, device=dev)
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+        rlk.rlk_logp_fwd(desc, inp.logits, inp.targets, mask_u8, logp, lse, ws,
+                         torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        per[str(s)] = {"logp": sha256_device(logp), "lse": sha256_device(lse)}
+        del ws
+    out["outputs_by_virtual_shards"] = per
+    out["outputs_identical_across_shards"] = len({(v["logp"], v["lse"]) for v in per.values()}) == 1
+    return out
 
 
 LMHEAD_WORKLOAD = "lmhead_b4096_k4096_v151936_p152576"
@@ -183,7 +273,8 @@ def cpu_baseline_lmhead(h, w, tgt, v_real: int, max_seconds: float) -> dict:
     import oracle
 
     orc = oracle.get()
-    cores = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    cores = host["threads"]
     n, k = h.shape
     hb = h.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     wb = w[:v_real].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -202,7 +293,7 @@ def cpu_baseline_lmhead(h, w, tgt, v_real: int, max_seconds: float) -> dict:
             "kind": "oracle",
             "sample": f"tokens 0..{done - 1} of the same workload ({done} of {n} tokens): "
                       f"h . W^T in fp64, then the fp64 log-softmax, {elapsed:.1f} s",
-            "tokens_per_s": round(done / elapsed, 3)}
+            "tokens_per_s": round(done / elapsed, 3), "host": host}
 
 
 def bench_lmhead(args) -> int:
@@ -295,6 +386,8 @@ def main() -> int:
                          "and entropy gradients) instead of rlk_logp_fwd + rlk_logp_bwd")
     ap.add_argument("--library-gemm", action="store_true",
                     help="LM-head workload: also time the library GEMM of the same shape")
+    ap.add_argument("--no-sha", action="store_true",
+                    help="skip the SHA-256 fingerprints of the inputs and of logp/LSE at S = 1, 8")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the stream-ceiling probe reported beside the roofline")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -444,6 +537,11 @@ def main() -> int:
         log(f"bench: copy probe {nbytes} bytes x3 done")
         del src, dst
 
+    shas = None
+    if not args.no_sha:
+        log("bench: SHA-256 of the inputs and of logp/LSE at S = 1 and 8")
+        shas = fingerprints(rlk, wl, inps[0], masks[0])
+
     if one_pass:
         total_bytes = algorithmic_bytes_one_pass(wl)
         value = total_bytes / (ms_step * 1e-3) / 1e9
@@ -512,6 +610,11 @@ def main() -> int:
         "tokens_per_s": round(n / (ms_step * 1e-3), 1),
         "step_ms_stream": step_spread,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        # the same step counted the way the workload's own description counts it:
+        # one read of every real logit and one write of every dX element
+        "hbm_frac_one_read": (round(algorithmic_bytes_one_pass(wl) / (ms_step * 1e-3) / 1e9
+                                    / HBM_PEAK_GBS, 4) if wl.backward and not extended
+                              else None),
         "algorithmic_bytes_per_step": total_bytes,
         "kernels": kernels,
         "roofline": roofline,
@@ -520,6 +623,7 @@ def main() -> int:
     if one_read is not None:
         line["one_read_accounting"] = one_read
     line["measured_ceilings"] = ceilings
+    line["sha256"] = shas
     print(json.dumps(line), flush=True)
     return 0
 

@@ -7,12 +7,12 @@
  *   [PR289] PR #289 "[WS2][PR4][Logp] feat: add distributed TP/CP logprob drift
  *           report": the stacked PR1 commit messages define the contract --
  *           padded vs real vocabulary, an explicit active mask plus
- *           ignore_index, padded columns masked to -inf before per-tile fp32
- *           (max, sumexp) partials, a (-inf, 0) identity partial for
- *           padding-only or all -inf tiles, a merge in fixed global tile order,
+ *           ignore_index, padding columns excluded from the per-tile fp32
+ *           (max, sumexp) partials, the (-inf, 0) partial of a tile that has
+ *           no finite real logit, a merge in fixed global tile order,
  *           and fp32 selected-logprob and fp32 LSE outputs.  The review excerpt
  *           of the op's apply() shows the target-range check on active tokens
- *           and the "non-finite logsumexp on an active row" error.
+ *           and the refusal of an active row whose LSE is not finite.
  *   [H100V] "H100 canonical TP/CP validation" (docs/usage/h100-matrix-validation.md):
  *           the RL runs whose log metrics include the mean entropy.
  *   [I323]  Issue #323 "[WS2][Logprob] H100 validation and reproduction guide
@@ -67,9 +67,9 @@
  *     large batch is split into several launches of at most 2^31 threads each
  *     (the backward of 152576-column rows, at 75 blocks of 128 threads per
  *     row, splits from 223K rows on).  The split never changes a result bit.
- *     The environment variable RLK_MAX_LAUNCH_THREADS (read at every call;
- *     values below 1024 count as 1024) lowers the limit, so that tests can
- *     check this on small inputs.
+ *     The environment variable RLK_MAX_LAUNCH_THREADS (read once per process,
+ *     at its first launch; values below 1024 count as 1024) lowers the limit,
+ *     so that tests can check this on small inputs.
  */
 #ifndef RLK_LOGP_H_
 #define RLK_LOGP_H_

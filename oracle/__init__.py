@@ -46,7 +46,7 @@ class OracleError(RuntimeError):
 
 def compile_oracle(src: Path, out: Path) -> Path:
     """Compile an oracle source with gcc (strict IEEE fp64: no fast-math, no contraction)."""
-    tmp = out.with_name(out.name + ".tmp")
+    tmp = out.with_name(f"{out.name}.tmp{os.getpid()}")  # parallel test workers may race
     subprocess.run(["gcc", *GCC_FLAGS, str(src), "-o", str(tmp), "-lpthread", "-lm"], check=True)
     os.replace(tmp, out)
     return out

@@ -10,7 +10,7 @@
  * Sources (web pages; cited by title and section):
  *   [PR289]  PR #289 "[WS2][PR4][Logp] feat: add distributed TP/CP logprob drift
  *            report" -- the stacked PR1 commit messages (contract: ShardingSpec,
- *            MaskSpec, ReductionSpec, the (-inf, 0) identity partial, padded
+ *            MaskSpec, ReductionSpec, (-inf, 0) as the identity partial, padded
  *            columns masked to -inf), the review excerpt of the op's apply()
  *            (target-range and non-finite-LSE checks), and the description's
  *            "Independent FP32 oracle" and "Comparison contract" sections.
@@ -29,8 +29,8 @@
  *
  * The tile decomposition of the pages is an exact regrouping of the LSE sum, so
  * the oracle takes the whole real vocabulary at once, as the pages' own oracle
- * does ([PR289] "Independent FP32 oracle": it computes directly from the
- * complete real vocabulary and does not reuse the sharded merge).  Arithmetic is
+ * does ([PR289] "Independent FP32 oracle": it works from the whole real
+ * vocabulary in one pass and never goes through the sharded merge).  Arithmetic is
  * fp64; the sum runs sequentially in ascending column order.
  *
  * Readings where the pages are silent (each also listed in the design notes):
@@ -44,7 +44,7 @@
  *     apply(): active targets are validated against the real vocabulary size);
  *     the oracle writes NaN for that row's logp and reports the first such row.
  *   - A non-finite LSE on an effective-active row is an error ([PR289] apply():
- *     logits over the real vocabulary must be finite for every active token).
+ *     such a row is refused).
  *
  * Side outputs and extra gradients (entropy_row, bwd_ex_row below):
  *
@@ -307,7 +307,7 @@ static void partials_row(const job* cjb, int64_t r, double* scratch) {
           a += exp(x[j] - m) * (x[j] - m);
         }
       }
-      /* m == -inf: the (-inf, 0) identity partial (and a = 0) */
+      /* m == -inf: no finite real logit, so (m, s, a) = (-inf, 0, 0) */
     }
     jb->pmax[r * jb->num_tiles + t] = m;
     jb->psum[r * jb->num_tiles + t] = s;

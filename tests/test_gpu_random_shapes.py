@@ -90,8 +90,10 @@ def test_random_shape(orc, c):
     gen = torch.Generator(device="cpu").manual_seed(c["seed"])
     gl, gh = (torch.randn(wl.num_tokens, generator=gen).to(DEV) for _ in range(2))
     dx = rlk.backward_ex(inp.logits, inp.targets, inp.mask, lse, ent, inp.grad, gl, gh, **kw)
-    dox = orc.bwd_ex(xb, tgt, mask, lse.double().cpu().numpy(), real_vocab=wl.real_vocab,
-                     padded_vocab=wl.padded_vocab, ent=ent.double().cpu().numpy(), g=g,
+    # the oracle's side takes the oracle's own LSE and entropy
+    dox = orc.bwd_ex(xb, tgt, mask, so, real_vocab=wl.real_vocab,
+                     padded_vocab=wl.padded_vocab, ent=orc.entropy(xb, real_vocab=wl.real_vocab),
+                     g=g,
                      g_lse=gl.double().cpu().numpy(), g_ent=gh.double().cpu().numpy(),
                      raise_on_error=False)
     P.check_bwd_ex(P.dlogits_host(dx), dox, np.zeros(wl.num_tokens, dtype=bool), wl.real_vocab,

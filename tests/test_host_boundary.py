@@ -325,21 +325,38 @@ def test_extended_forward_and_backward_host_validation():
                         1024, f32, None, stream=s)
 
 
-def test_launch_thread_limit_reads_its_environment_variable(monkeypatch):
+_LIMIT_PROBE = r"""
+import ctypes, os, sys
+lib = ctypes.CDLL(sys.argv[1])
+fn = getattr(lib, "_ZN3rlk19launch_thread_limitEv")
+fn.restype = ctypes.c_int64
+first = fn()
+os.environ["RLK_MAX_LAUNCH_THREADS"] = "2048"  # too late: read once per process
+print(first, fn())
+"""
+
+
+def test_launch_thread_limit_reads_its_environment_variable_once():
     """The per-launch thread limit (a dispatch's grid size is 32 bits of threads): 2^31 by
     default, lowered by RLK_MAX_LAUNCH_THREADS (the hook the split-launch GPU test uses),
-    never below 1024 threads, never above 2^31, and a value that is not a number is ignored."""
+    never below 1024 threads, never above 2^31, a value that is not a number is ignored,
+    and the variable is read once per process, at the first launch."""
+    import os
+    import subprocess
+    import sys
+
     lib = ctypes.CDLL(str(rlk.LIB_PATH))
-    fn = getattr(lib, "_ZN3rlk19launch_thread_limitEv", None)
-    if fn is None:
+    if getattr(lib, "_ZN3rlk19launch_thread_limitEv", None) is None:
         pytest.skip("internal symbol not exported")
-    fn.restype = ctypes.c_int64
-    monkeypatch.delenv("RLK_MAX_LAUNCH_THREADS", raising=False)
-    assert fn() == 1 << 31
-    for value, want in (("5000", 5000), ("10", 1024), (str(1 << 40), 1 << 31), ("abc", 1 << 31),
-                        ("", 1 << 31)):
-        monkeypatch.setenv("RLK_MAX_LAUNCH_THREADS", value)
-        assert fn() == want, value
+    for value, want in ((None, 1 << 31), ("5000", 5000), ("10", 1024), (str(1 << 40), 1 << 31),
+                        ("abc", 1 << 31), ("", 1 << 31)):
+        env = {k: v for k, v in os.environ.items() if k != "RLK_MAX_LAUNCH_THREADS"}
+        if value is not None:
+            env["RLK_MAX_LAUNCH_THREADS"] = value
+        r = subprocess.run([sys.executable, "-c", _LIMIT_PROBE, str(rlk.LIB_PATH)], env=env,
+                           capture_output=True, text=True, timeout=120, check=True)
+        first, later = (int(x) for x in r.stdout.split())
+        assert first == want and later == want, (value, r.stdout)
 
 
 def test_conveniences_check_tensors_before_anything_runs():

@@ -96,6 +96,31 @@ def pin_geometry(o):
             assert f[0] == 0 and f[-1] == t
             assert set(np.diff(f)) <= {t // s, -(-t // s)} and (np.diff(f) >= 1).all()
     assert list(np.diff(o.shard_tiles(64, 4))) == [16] * 4
+    # Reading R1/R2 (floor, remainder toward the last tile): where T does not
+    # divide V the narrow tiles come first and the last tile is the widest, so
+    # the last bound is the one the remainder moves.  Exact values, then a
+    # brute-force search of the definition "largest b with b * T <= t * V"
+    # (no integer division) on small non-divisible sizes.  A ceiling reading
+    # gives [0, 4, 7, 10] and [0, 3, 5, 7] here.
+    assert list(o.tile_bounds(10, 3)) == [0, 3, 6, 10]
+    assert list(o.tile_bounds(7, 4)) == [0, 1, 3, 5, 7]
+    assert list(o.tile_bounds(152577, 64)[:3]) == [0, 2384, 4768]
+    assert list(o.shard_tiles(7, 3)) == [0, 2, 4, 7]
+    assert list(o.shard_tiles(64, 3)) == [0, 21, 42, 64]
+
+    def largest_multiple_below(t, v, tt):
+        b = 0
+        while (b + 1) * tt <= t * v:
+            b += 1
+        return b
+
+    for v, t in [(10, 3), (7, 4), (23, 5), (100, 7), (129, 8), (37, 36), (61, 9)]:
+        want = [largest_multiple_below(i, v, t) for i in range(t + 1)]
+        assert list(o.tile_bounds(v, t)) == want, (v, t)
+        if t >= 2:
+            s = max(1, t // 3 + 1)
+            want_s = [largest_multiple_below(i, t, s) for i in range(s + 1)]
+            assert list(o.shard_tiles(t, s)) == want_s, (t, s)
     for bad in ((0, 1), (5, 0), (5, 6)):
         with pytest.raises(oracle.OracleError):
             o.tile_bounds(*bad)
@@ -479,6 +504,11 @@ MUTANTS = {
     "bf16_shift": ("uint32_t w = (uint32_t)bits << 16;", "uint32_t w = (uint32_t)bits << 15;"),
     "bounds_truncated": ("bounds[t] = (padded_vocab * (int64_t)t) / (int64_t)num_tiles;",
                          "bounds[t] = (padded_vocab / (int64_t)num_tiles) * (int64_t)t;"),
+    "bounds_ceil": ("bounds[t] = (padded_vocab * (int64_t)t) / (int64_t)num_tiles;",
+                    "bounds[t] = (padded_vocab * (int64_t)t + num_tiles - 1) / (int64_t)num_tiles;"),
+    "shards_ceil": ("first_tile[s] = (int32_t)(((int64_t)s * num_tiles) / num_shards);",
+                    "first_tile[s] = (int32_t)(((int64_t)s * num_tiles + num_shards - 1) / "
+                    "num_shards);"),
     "onehot_dropped": ("double onehot = (j == (int64_t)t) ? 1.0 : 0.0;",
                        "double onehot = 0.0;"),
     "identity_partial_wrong": ("double m = -INFINITY, s = 0.0, a = 0.0;",

@@ -6,10 +6,10 @@
 // library allocates nothing; its only state is the per-thread detail string.
 //
 // Error semantics follow PR #289 "[WS2][PR4][Logp] feat: add distributed TP/CP
-// logprob drift report": dispatch is fail-closed (PR1 commit messages: no
-// silent fallback), and the op rejects active targets outside the real
-// vocabulary and a non-finite logsumexp on an active row (review excerpt of
-// the op's apply()).
+// logprob drift report": dispatch is fail-closed (PR1 commit messages: a backend
+// that cannot run is an error, never replaced by another), and the op refuses
+// an active target beyond the real vocabulary and an active row whose LSE is
+// not finite (review excerpt of the op's apply()).
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -103,8 +103,8 @@ rlk_status finish_validate(uint32_t* status, hipStream_t stream, bool check_nonf
                 "an effective-active target is outside [0, real_vocab); its outputs are NaN");
   if (check_nonfinite && host[1])
     return fail(RLK_ERR_NONFINITE_LSE,
-                "non-finite logsumexp on an effective-active row: logits over the real "
-                "vocabulary must be finite for every active token");
+                "an effective-active row has a non-finite LSE (its real logits are all "
+                "-inf, or one of them is NaN or +inf)");
   return ok();
 }
 
@@ -597,7 +597,9 @@ const char* rlk_last_error_detail(void) { return g_detail.c_str(); }
 
 namespace rlk {
 
-int64_t launch_thread_limit() {
+namespace {
+
+int64_t read_thread_limit() {
   constexpr int64_t kLimit = int64_t{1} << 31;
   const char* v = getenv("RLK_MAX_LAUNCH_THREADS");
   if (!v || !*v) return kLimit;
@@ -606,6 +608,15 @@ int64_t launch_thread_limit() {
   if (end == v) return kLimit;  // not a number: the default
   if (n < 1024) return 1024;    // at least two blocks of every kernel
   return n < kLimit ? (int64_t)n : kLimit;
+}
+
+}  // namespace
+
+// The environment is read once, at the first launch of the process (a
+// function-local static: initialised once, safely under concurrent first calls).
+int64_t launch_thread_limit() {
+  static const int64_t limit = read_thread_limit();
+  return limit;
 }
 
 }  // namespace rlk

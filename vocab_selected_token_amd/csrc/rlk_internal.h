@@ -114,8 +114,8 @@ struct LmheadArgs {
 // of threads: at 2^32 the launch fails, and above it the size wraps around and
 // the kernel silently runs on a fraction of the grid.  Every launcher splits
 // its work into launches of at most this many threads (2^31, or less when the
-// RLK_MAX_LAUNCH_THREADS environment variable says so -- a hook for tests, which
-// check that any split gives the same bits).
+// RLK_MAX_LAUNCH_THREADS environment variable says so at the process's first
+// launch -- a hook for tests, which check that any split gives the same bits).
 int64_t launch_thread_limit();
 
 int64_t stage1_blocks(int64_t items);

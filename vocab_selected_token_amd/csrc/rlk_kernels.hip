@@ -14,7 +14,7 @@
 //
 // Sources (web pages, by title and section): PR #289 "[WS2][PR4][Logp] feat:
 // add distributed TP/CP logprob drift report", stacked PR1 commit messages
-// (padded columns masked to -inf before the local (max, sumexp) partials; the
+// (padding columns take no part in any tile's (max, sumexp) statistic; the
 // (-inf, 0) identity partial; fp32 merge in fixed global tile order; fp32 logp
 // and LSE outputs) and the review excerpt of the op's apply() (active-target
 // range check, non-finite-LSE check).  Issue #323 "[WS2][Logprob] H100
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kWPB * 64) void stage1_partials(
 // Stage 2: per-row merge in ascending tile order, target gather, mask.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 64;  // one row per lane; small blocks spread rows over every CU
-constexpr int kMergeVec = 64;      // tiles held in registers by the vectorised path
+constexpr int kMergeVec = 64;      // most tiles the vectorised (16-byte load) path takes
 
 // The merge accumulates S = sum_t s_t exp(m_t - M) in fp64, in ascending tile
 // order: a running fp32 sum of T terms drifts by up to T half-ulps, which at
@@ -399,33 +399,34 @@ __device__ __forceinline__ float lse_of(float M, double S) {
 // the identity.  pm/ps point at the row's T values.
 __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
                                            const float* __restrict__ ps, int32_t num_tiles) {
+  float M = kNegInf;
+  double S = 0.0;
   if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
-    // same arithmetic, with the loads issued up front as 16-byte vectors
-    float mv[kMergeVec], sv[kMergeVec];
+    // the same arithmetic with 16-byte loads: every maximum in flight at once,
+    // then the sum over four tiles per load of each array, a few loads ahead
+    // (a row's partials are in the cache by then; holding all 2T values in
+    // registers cost 201 VGPRs)
 #pragma unroll
     for (int t = 0; t < kMergeVec; t += 4) {
       if (t < num_tiles) {
         const float4 a = *reinterpret_cast<const float4*>(pm + t);
-        const float4 b = *reinterpret_cast<const float4*>(ps + t);
-        mv[t] = a.x; mv[t + 1] = a.y; mv[t + 2] = a.z; mv[t + 3] = a.w;
-        sv[t] = b.x; sv[t + 1] = b.y; sv[t + 2] = b.z; sv[t + 3] = b.w;
+        M = maxnan(M, a.x); M = maxnan(M, a.y); M = maxnan(M, a.z); M = maxnan(M, a.w);
       }
     }
-    float M = kNegInf;
-#pragma unroll
-    for (int t = 0; t < kMergeVec; ++t)
-      if (t < num_tiles) M = maxnan(M, mv[t]);
     if (M == kNegInf) return kNegInf;
-    double S = 0.0;
+#pragma unroll 2
+    for (int32_t t = 0; t < num_tiles; t += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(pm + t);
+      const float4 b = *reinterpret_cast<const float4*>(ps + t);
+      const float mv[4] = {a.x, a.y, a.z, a.w}, sv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int t = 0; t < kMergeVec; ++t)
-      if (t < num_tiles && mv[t] != kNegInf) S = fma((double)sv[t], (double)expf(mv[t] - M), S);
+      for (int j = 0; j < 4; ++j)
+        if (mv[j] != kNegInf) S = fma((double)sv[j], (double)expf(mv[j] - M), S);
+    }
     return lse_of(M, S);
   }
-  float M = kNegInf;
   for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
   if (M == kNegInf) return kNegInf;
-  double S = 0.0;
   for (int32_t t = 0; t < num_tiles; ++t) {
     const float mt = pm[t];
     if (mt != kNegInf) S = fma((double)ps[t], (double)expf(mt - M), S);
@@ -438,6 +439,16 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ pm,
 // s_t), which is sum_j exp(x_j - M) (x_j - M) over the row.  Then LSE = M + log S
 // (the same bits as merge_row) and H = log S - A / S, rounded to fp32 once; H is
 // NaN where LSE is not finite (no distribution).
+__device__ __forceinline__ void merge_step_entropy(float mt, float st, float at, float M,
+                                                   double& S, double& A) {
+  if (mt != kNegInf) {
+    const float d = mt - M;
+    const double e = (double)expf(d);
+    S = fma((double)st, e, S);
+    A = fma(e, fma((double)d, (double)st, (double)at), A);
+  }
+}
+
 __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
                                                    const float* __restrict__ ps,
                                                    const float* __restrict__ pa,
@@ -446,44 +457,29 @@ __device__ __forceinline__ float merge_row_entropy(const float* __restrict__ pm,
   float M = kNegInf;
   double S = 0.0, A = 0.0;
   if (num_tiles <= kMergeVec && (num_tiles & 3) == 0) {
-    // same arithmetic, with the loads issued up front as 16-byte vectors
-    float mv[kMergeVec], sv[kMergeVec], av[kMergeVec];
+    // the same arithmetic with 16-byte loads, as in merge_row
 #pragma unroll
     for (int t = 0; t < kMergeVec; t += 4) {
       if (t < num_tiles) {
-        const float4 a4 = *reinterpret_cast<const float4*>(pm + t);
-        const float4 b4 = *reinterpret_cast<const float4*>(ps + t);
-        const float4 c4 = *reinterpret_cast<const float4*>(pa + t);
-        mv[t] = a4.x; mv[t + 1] = a4.y; mv[t + 2] = a4.z; mv[t + 3] = a4.w;
-        sv[t] = b4.x; sv[t + 1] = b4.y; sv[t + 2] = b4.z; sv[t + 3] = b4.w;
-        av[t] = c4.x; av[t + 1] = c4.y; av[t + 2] = c4.z; av[t + 3] = c4.w;
+        const float4 a = *reinterpret_cast<const float4*>(pm + t);
+        M = maxnan(M, a.x); M = maxnan(M, a.y); M = maxnan(M, a.z); M = maxnan(M, a.w);
       }
     }
-#pragma unroll
-    for (int t = 0; t < kMergeVec; ++t)
-      if (t < num_tiles) M = maxnan(M, mv[t]);
     if (M == kNegInf) return kNegInf;
-#pragma unroll
-    for (int t = 0; t < kMergeVec; ++t) {
-      if (t < num_tiles && mv[t] != kNegInf) {
-        const float d = mv[t] - M;
-        const double e = (double)expf(d);
-        S = fma((double)sv[t], e, S);
-        A = fma(e, fma((double)d, (double)sv[t], (double)av[t]), A);
-      }
+#pragma unroll 2
+    for (int32_t t = 0; t < num_tiles; t += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(pm + t);
+      const float4 b4 = *reinterpret_cast<const float4*>(ps + t);
+      const float4 c4 = *reinterpret_cast<const float4*>(pa + t);
+      merge_step_entropy(a4.x, b4.x, c4.x, M, S, A);
+      merge_step_entropy(a4.y, b4.y, c4.y, M, S, A);
+      merge_step_entropy(a4.z, b4.z, c4.z, M, S, A);
+      merge_step_entropy(a4.w, b4.w, c4.w, M, S, A);
     }
   } else {
     for (int32_t t = 0; t < num_tiles; ++t) M = maxnan(M, pm[t]);
     if (M == kNegInf) return kNegInf;
-    for (int32_t t = 0; t < num_tiles; ++t) {
-      const float mt = pm[t];
-      if (mt != kNegInf) {
-        const float d = mt - M;
-        const double e = (double)expf(d);
-        S = fma((double)ps[t], e, S);
-        A = fma(e, fma((double)d, (double)ps[t], (double)pa[t]), A);
-      }
-    }
+    for (int32_t t = 0; t < num_tiles; ++t) merge_step_entropy(pm[t], ps[t], pa[t], M, S, A);
   }
   const float L = lse_of(M, S);
   if (__builtin_isfinite(L)) H = (float)(log(S) - A / S);
@@ -833,7 +829,9 @@ __device__ __forceinline__ float merge_lanes_entropy(float mt, float st, float a
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   double S = 0.0, A = 0.0;
-#pragma unroll
+  // two groups of LDS loads ahead: fully unrolled, all 256 values were held
+  // in registers at once (256 VGPRs, occupancy 1)
+#pragma unroll 2
   for (int t = 0; t < 64; t += 4) {
     const float4 e4 = *reinterpret_cast<const float4*>(s_e + t);
     const float4 s4 = *reinterpret_cast<const float4*>(s_sv + t);
