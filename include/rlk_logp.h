@@ -172,6 +172,24 @@ rlk_status rlk_logp_bwd(const rlk_logp_desc* desc, const void* logits, const int
                         void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* rlk_logp_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a device array of the library's
+ * own, one per GPU, of 32 MiB + 256 bytes, held until the process ends; the
+ * call allocates nothing and frees nothing.  Outputs are bitwise those of
+ * rlk_logp_fwd on the same arguments.
+ *   desc, logits, targets, active_mask, logp, lse   as for rlk_logp_fwd.
+ * Limit: rlk_logp_workspace_bytes(desc) <= 32 MiB + 256, i.e.
+ * num_tokens * num_vocab_tiles <= 4,194,304 (65,536 rows of 64 tiles); a larger
+ * problem returns RLK_ERR_WORKSPACE before anything is enqueued.  Every call on
+ * one GPU uses the same array: calls that overlap on one GPU (from two host
+ * threads, or on two streams without ordering between them) race and must not
+ * be made.  Its first call on a device looks up the array's address there (no
+ * allocation); other errors as for rlk_logp_fwd. */
+rlk_status rlk_logp_fwd_noalloc(const rlk_logp_desc* desc, const void* logits,
+                                const int32_t* targets, const uint8_t* active_mask, float* logp,
+                                float* lse, void* stream);
+
 /* Extended forward: rlk_logp_fwd plus the per-row entropy of the softmax over
  * the real vocabulary,
  *   H_r = -sum_{j < V_real} p_rj log p_rj,  p_rj = exp(x_rj - LSE_r),  0 log 0 = 0.

@@ -396,3 +396,29 @@ def test_conveniences_check_tensors_before_anything_runs():
                          torch.zeros(v - 1, 64, dtype=torch.bfloat16), t32, real_vocab=v)
     with pytest.raises(TypeError, match="int32"):
         rlk.selected_token_logprob(x, t32.long(), real_vocab=v, num_vocab_tiles=4)
+
+
+def test_noalloc_forward_host_validation():
+    """rlk_logp_fwd_noalloc: descriptor errors as rlk_logp_fwd; a problem whose
+    workspace exceeds the fixed 32 MiB + 256 bytes scratch is refused with
+    RLK_ERR_WORKSPACE before anything touches a device; an empty batch is a no-op."""
+    import torch
+
+    s = torch.cuda.current_stream() if torch.cuda.is_available() else None
+
+    def call(d):
+        return rlk._lib.rlk_logp_fwd_noalloc(ctypes.byref(d), None, None, None, None, None,
+                                             None if s is None else s.cuda_stream)
+
+    assert call(desc(num_vocab_tiles=0)) == rlk.RLK_ERR_BAD_TILING
+    assert call(desc(num_tokens=-1)) == rlk.RLK_ERR_BAD_SHAPE
+    assert call(desc(num_tokens=0)) == rlk.RLK_OK
+    # 65,537 rows of 64 tiles need 256 + 2 * 16,777,472 bytes: one row too many
+    big = desc(num_tokens=65537, real_vocab=151936, padded_vocab=152576, ld_logits=152576)
+    assert rlk.rlk_logp_workspace_bytes(big) > (32 << 20) + 256
+    assert call(big) == rlk.RLK_ERR_WORKSPACE
+    assert "32" in rlk.rlk_last_error_detail() or "scratch" in rlk.rlk_last_error_detail()
+    fits = desc(num_tokens=65536, real_vocab=151936, padded_vocab=152576, ld_logits=152576)
+    assert rlk.rlk_logp_workspace_bytes(fits) == (32 << 20) + 256
+    if not torch.cuda.is_available():  # no device to look the scratch up on
+        assert call(fits) == rlk.RLK_ERR_HIP

@@ -38,7 +38,8 @@ EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd",
             "rlk_logp_ex_workspace_bytes", "rlk_logp_fwd_ex", "rlk_logp_bwd_ex",
             "rlk_logp_fwd_bwd_workspace_bytes", "rlk_logp_fwd_bwd",
             "rlk_logp_fused_lmhead_workspace_bytes", "rlk_logp_fused_lmhead",
-            "rlk_logp_tile_geometry", "rlk_status_string", "rlk_last_error_detail")
+            "rlk_logp_tile_geometry", "rlk_status_string", "rlk_last_error_detail",
+            "rlk_logp_fwd_noalloc")
 
 
 class rlk_logp_desc(ctypes.Structure):  # noqa: N801 - mirrors the C struct name
@@ -66,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.rlk_logp_workspace_bytes.restype = sz
     lib.rlk_logp_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rlk_logp_fwd.restype = ctypes.c_int
+    lib.rlk_logp_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.rlk_logp_fwd_noalloc.restype = ctypes.c_int
     lib.rlk_logp_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz, vp]
     lib.rlk_logp_bwd.restype = ctypes.c_int
     lib.rlk_logp_ex_workspace_bytes.argtypes = [dp]
@@ -128,6 +131,11 @@ def rlk_logp_fwd(desc, logits, targets, active_mask, logp, lse, workspace, strea
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.rlk_logp_fwd(ctypes.byref(desc), _ptr(logits), _ptr(targets), _ptr(active_mask),
                              _ptr(logp), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rlk_logp_fwd_noalloc(desc, logits, targets, active_mask, logp, lse, stream=None) -> None:
+    _check(_lib.rlk_logp_fwd_noalloc(ctypes.byref(desc), _ptr(logits), _ptr(targets),
+                                     _ptr(active_mask), _ptr(logp), _ptr(lse), _stream(stream)))
 
 
 def rlk_logp_bwd(desc, logits, targets, active_mask, lse, grad_logp, dlogits, ld_dlogits: int,

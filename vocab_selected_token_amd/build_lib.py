@@ -32,16 +32,19 @@ def build() -> Path:
     k_obj = obj_dir / "rlk_kernels.o"
     l_obj = obj_dir / "rlk_lmhead.o"
     b_obj = obj_dir / "rlk_boundary.o"
+    n_obj = obj_dir / "rlk_noalloc.o"
     subprocess.run([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / "rlk_kernels.hip"),
                     "-o", str(k_obj)], check=True)
     subprocess.run([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / "rlk_lmhead.hip"),
                     "-o", str(l_obj)], check=True)
+    subprocess.run([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / "rlk_noalloc.hip"),
+                    "-o", str(n_obj)], check=True)
     subprocess.run([HIPCC, "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
                     "-I/opt/rocm/include", *inc, "-c", str(CSRC / "rlk_boundary.cpp"),
                     "-o", str(b_obj)], check=True)
     tmp = LIB.with_name(LIB.name + ".tmp")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", str(k_obj), str(l_obj),
-                    str(b_obj),
+                    str(n_obj), str(b_obj),
                     "-o", str(tmp)], check=True)
     os.replace(tmp, LIB)
     tmp = CALIB.with_name(CALIB.name + ".tmp")

@@ -232,6 +232,27 @@ rlk_status rlk_logp_fwd(const rlk_logp_desc* desc, const void* logits, const int
                      workspace_bytes, stream_ptr);
 }
 
+rlk_status rlk_logp_fwd_noalloc(const rlk_logp_desc* desc, const void* logits,
+                                const int32_t* targets, const uint8_t* active_mask, float* logp,
+                                float* lse, void* stream_ptr) {
+  rlk_status st = check_desc(desc);
+  if (st != RLK_OK) return st;
+  if (desc->num_tokens == 0) return ok();
+  const size_t need = needed_workspace(desc);
+  if (need > rlk::kNoAllocScratchBytes)
+    return fail(RLK_ERR_WORKSPACE,
+                "rlk_logp_fwd_noalloc needs %zu bytes of scratch for num_tokens=%lld x "
+                "num_vocab_tiles=%d; its fixed scratch holds %zu (use rlk_logp_fwd with a "
+                "caller-allocated workspace)",
+                need, (long long)desc->num_tokens, desc->num_vocab_tiles,
+                rlk::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = rlk::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  return run_forward(desc, logits, targets, active_mask, logp, lse, nullptr, ws,
+                     rlk::kNoAllocScratchBytes, stream_ptr);
+}
+
 size_t rlk_logp_ex_workspace_bytes(const rlk_logp_desc* desc) {
   if (check_desc(desc) != RLK_OK) return 0;
   return needed_workspace_ex(desc);

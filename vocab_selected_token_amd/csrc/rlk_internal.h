@@ -118,6 +118,13 @@ struct LmheadArgs {
 // launch -- a hook for tests, which check that any split gives the same bits).
 int64_t launch_thread_limit();
 
+// The allocation-free forward's workspace: a device array of the library's own,
+// one per GPU, of this many bytes (status words plus 2 * N * T fp32 partials:
+// N * T <= 4,194,304, e.g. 65,536 rows of 64 tiles).
+constexpr size_t kNoAllocScratchBytes = (size_t{32} << 20) + 256;
+// Its device address on the current device (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 int64_t stage1_blocks(int64_t items);
 int64_t lmhead_grid_blocks(int32_t num_tokens, int32_t real_vocab);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
