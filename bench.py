@@ -98,7 +98,9 @@ def measured_ceilings():
     except (subprocess.SubprocessError, ValueError, IndexError):
         return None
     out["source"] = ("rlk_calib: 8 GiB streams, 16-byte nontemporal loads/stores, "
-                     "1 KB per wave instruction, median of 7")
+                     "1 KB per wave instruction; row_copy and slice_copy copy 32768 rows of "
+                     "305,152 bytes one row per block / one sixteenth of a row per block; "
+                     "median of 7")
     return out
 
 
@@ -521,10 +523,20 @@ def main() -> int:
         b_one = algorithmic_bytes_one_pass(wl)
         one_read = {"bytes_per_step": b_one,
                     "two_calls_GB/s": round(b_one / (ms_step * 1e-3) / 1e9, 1),
+                    "two_calls_hbm_frac": round(b_one / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "one_launch_ms_per_step": round(ms_one, 4),
                     "one_launch_GB/s": round(b_one / (ms_one * 1e-3) / 1e9, 1),
                     "one_launch_hbm_frac": round(b_one / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "one_launch_tokens_per_s": round(n / (ms_one * 1e-3), 1)}
+        if ceilings is not None and "row_copy_GBps" in ceilings:
+            # what a copy of the same bytes takes on this GPU in the two shapes such a
+            # schedule can have, with no arithmetic at all (rlk_calib)
+            one_read["row_copy_ms"] = round(b_one / (ceilings["row_copy_GBps"] * 1e9) * 1e3, 4)
+            one_read["slice_copy_ms"] = round(b_one / (ceilings["slice_copy_GBps"] * 1e9) * 1e3,
+                                              4)
+            one_read["one_launch_frac_of_row_copy"] = round(one_read["row_copy_ms"] / ms_one, 4)
+            one_read["slice_copy_hbm_frac"] = round(ceilings["slice_copy_GBps"] / HBM_PEAK_GBS,
+                                                    4)
         log(f"bench: one-launch schedule {ms_one:.3f} ms/step")
 
     if args.copy_probe_gib > 0:  # plain copy kernel of known size, for counter scaling

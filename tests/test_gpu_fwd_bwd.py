@@ -123,6 +123,48 @@ def test_small_parity_and_bitwise_equality(orc, case):
             assert_same_bits(fused(inp, dt, shards=s), out, f"{case} {dt} S={s}")
 
 
+# Larger batches of ragged shapes, with T above 64 (the merge from LDS),
+# all-padding tiles and rows without a finite logit or holding a NaN.
+LARGER = [
+    dict(n=1024, real=1000, pad=1000, T=7),
+    dict(n=1031, real=5000, pad=5120, ld=5128, T=64),
+    dict(n=1300, real=9000, pad=9000, T=65),
+    dict(n=1500, real=4000, pad=4096, T=1024),
+    dict(n=1029, real=300, pad=1024, T=1024),
+    dict(n=2100, real=2374 * 3 + 1, pad=2374 * 3 + 8, T=3, spike=True),
+]
+
+
+@pytest.mark.parametrize("case", LARGER, ids=lambda c: f"n{c['n']}_v{c['real']}_p{c['pad']}_T{c['T']}")
+def test_larger_batches_parity_and_bitwise_equality(orc, case):
+    print(f"case {case}", flush=True)
+    wl = W.small_workload(case["n"], case["real"], case["pad"], ld=case.get("ld"),
+                          num_tiles=case["T"], spike_frac=0.3 if case.get("spike") else 0.0,
+                          spike=12.0, seed=case["n"] + 3000)
+    inp = W.make_inputs(wl, DEV)
+    inp.logits[5, :wl.real_vocab] = float("-inf")  # no finite logit: LSE -inf
+    inp.logits[6, min(3, wl.real_vocab - 1)] = float("nan")
+    inp.mask[5] = False
+    inp.mask[6] = False
+    for dt in (torch.float32, torch.bfloat16):
+        out = fused(inp, dt)
+        ref = separate(inp, dt)
+        for a, b, name in zip(out, ref, ("logp", "lse", "dlogits")):
+            na, nb = torch.isnan(a), torch.isnan(b)
+            assert torch.equal(na, nb), f"{case} {dt} {name}: NaN pattern differs"
+            assert torch.equal(bits(a)[~na], bits(b)[~nb]), f"{case} {dt} {name}: bits differ"
+        keep = torch.ones(wl.num_tokens, dtype=torch.bool, device=DEV)
+        keep[5:7] = False
+        rows = torch.nonzero(keep).flatten().cpu().numpy()
+        check_oracle(orc, inp, out, dt, f"{case} {dt}", rows=rows)
+        for s in sorted({2, 8, case["T"]} & set(range(2, case["T"] + 1))):
+            o2 = fused(inp, dt, shards=s)
+            for a, b, name in zip(o2, out, ("logp", "lse", "dlogits")):
+                na = torch.isnan(a)
+                assert torch.equal(na, torch.isnan(b)) and torch.equal(bits(a)[~na],
+                                                                      bits(b)[~na]), f"S={s} {name}"
+
+
 def test_empty_batch():
     wl = W.small_workload(0, 100)
     inp = W.make_inputs(wl, DEV)
