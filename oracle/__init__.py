@@ -228,6 +228,21 @@ class Oracle:
             raise OracleError(rc, -1)
         return z
 
+    def lmhead_logits_blas(self, h, w, *, real_vocab: int) -> np.ndarray:
+        """z = h . W^T over W's first real_vocab rows, as lmhead_logits computes it, with
+        numpy's float64 matrix product as the one step (fast enough for the 4096-token
+        workload in full; the plain-loop form pins it).  Decoding a bf16 pattern is exact:
+        its 16 bits are the top half of an IEEE binary32."""
+        h = np.ascontiguousarray(np.asarray(h))
+        w = np.ascontiguousarray(np.asarray(w))
+        if h.dtype != np.uint16 or w.dtype != np.uint16 or h.ndim != 2 or w.ndim != 2:
+            raise TypeError("h and W must be 2-D bf16 bit patterns (uint16)")
+        if h.shape[1] != w.shape[1] or w.shape[0] < real_vocab:
+            raise ValueError("h [N, K] and W [>= real_vocab, K] must share K")
+        hd = (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        wd = (w[:real_vocab].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return hd @ wd.T
+
     def lmhead_fwd(self, h, w, tgt, mask=None, *, real_vocab: int, ignore_index: int = -100,
                    nthreads: int = 0, raise_on_error: bool = True):
         """Selected-token logp and LSE of z = h . W^T (fp64): (logp, lse, status, bad_row)."""

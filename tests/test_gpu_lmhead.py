@@ -2,6 +2,8 @@
 fp64, then the full-vocabulary log-softmax).  Needs an MI355X."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -158,6 +160,44 @@ def test_fused_virtual_shards_bitwise(c):
                 P.effective_active(t_h, m_h), str(c))
 
 
+def draw_shard_cases(count: int, seed: int):
+    """Seeded ragged shapes for the virtual-shard check: tokens 1-513, K of 64-192,
+    256-9000 real columns, 0-1000 padded weight rows of random bits, two to five
+    shard counts up to T."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        v_real = int(rng.integers(256, 9001))
+        v_pad = v_real + int(rng.integers(0, 1001))
+        tiles = int(rng.integers(1, v_pad // 256 + 1))
+        shards = sorted({int(x) for x in rng.integers(1, tiles + 1, size=int(rng.integers(2, 6)))})
+        out.append(dict(i=i, n=int(rng.integers(1, 514)), k=int(rng.choice([64, 128, 192])),
+                        v_real=v_real, v_pad=v_pad, tiles=tiles, shards=shards))
+    return out
+
+
+# RLK_LMHEAD_SHARD_SWEEP=80 runs the longer sweep the design notes quote
+SHARD_SWEEP = draw_shard_cases(int(os.environ.get("RLK_LMHEAD_SHARD_SWEEP", "12")), seed=8080)
+
+
+@pytest.mark.parametrize("c", SHARD_SWEEP,
+                         ids=lambda c: "{i}_n{n}_k{k}_v{v_real}_p{v_pad}_T{tiles}".format(**c))
+def test_fused_virtual_shards_sweep(c):
+    """Every drawn shard count gives the bits of S = 1: logp, LSE and every partial."""
+    print(f"case {c}", flush=True)
+    n, t = c["n"], c["tiles"]
+    h, w, tgt, mask = make_case(n, c["k"], c["v_real"], c["v_pad"], seed=9000 + c["i"])
+    ref = run(h, w, tgt, mask, c["v_real"], c["v_pad"], t)
+    ref_bits = (ref[0].view(torch.int32).cpu(), ref[1].view(torch.int32).cpu()) + \
+        partials(ref[2], n, t)
+    for s in c["shards"]:
+        got = run(h, w, tgt, mask, c["v_real"], c["v_pad"], t, shards=s)
+        got_bits = (got[0].view(torch.int32).cpu(), got[1].view(torch.int32).cpu()) + \
+            partials(got[2], n, t)
+        for name, a, b in zip(("logp", "lse", "pmax", "psum"), ref_bits, got_bits):
+            assert torch.equal(a, b), f"{name} differs at S={s}"
+
+
 def test_fused_repeat_and_batch_invariance():
     h, w, tgt, mask = make_case(300, 128, 2500, 2560, seed=3)
     a = run(h, w, tgt, mask, 2500, 2560, 10)
@@ -182,25 +222,32 @@ def test_fused_validate_bad_target():
         assert torch.isfinite(logp[torch.arange(40, device=DEV) != 7]).all()
 
 
-def test_fused_lmhead_4096_sampled():
+def test_fused_lmhead_4096_full():
     """The LM-head workload: hidden [4096, 4096] ~ N(0,1), W [152576, 4096] ~ N(0, 0.02^2),
-    rows >= 151936 padding, 64 tiles, all tokens active; sampled tokens vs the oracle."""
+    rows >= 151936 padding, 64 tiles, all tokens active; every token against the oracle
+    (z = h . W^T in fp64 by matrix product, in blocks of 512 tokens, then the fp64
+    log-softmax)."""
     n, k, v_real, v_pad = 4096, 4096, 151936, 152576
     g = torch.Generator(device=DEV).manual_seed(123)
     h = torch.randn((n, k), generator=g, device=DEV).to(torch.bfloat16)
     w = (torch.randn((v_pad, k), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
     tgt = torch.randint(0, v_real, (n,), generator=g, device=DEV, dtype=torch.int32)
     logp, lse, _ = run(h, w, tgt, None, v_real, v_pad, 64)
-    rows = np.array(sorted({0, 1, 255, 256, 2047, 4095} |
-                           set(np.random.default_rng(0).choice(n, 26, replace=False).tolist())))
     o = oracle.get()
-    z = o.lmhead_logits(bf16_bits(h[torch.from_numpy(rows).to(DEV)]), bf16_bits(w),
-                        real_vocab=v_real)
-    t_h = tgt.cpu().numpy()[rows]
-    lo, so, _, _ = o.fwd(z, t_h, None, real_vocab=v_real)
-    stats = P.check_fwd(logp.cpu().numpy()[rows], lse.cpu().numpy()[rows], lo, so,
-                        np.ones(len(rows), bool), "lmhead 4096")
-    print(stats, flush=True)
+    wb = bf16_bits(w)
+    hb = bf16_bits(h)
+    t_all = tgt.cpu().numpy()
+    lp_all, ls_all = logp.cpu().numpy(), lse.cpu().numpy()
+    worst = {"lse_max_abs": 0.0, "logp_max_abs": 0.0}
+    for r0 in range(0, n, 512):
+        r1 = min(n, r0 + 512)
+        z = o.lmhead_logits_blas(hb[r0:r1], wb, real_vocab=v_real)
+        lo, so, _, _ = o.fwd(z, t_all[r0:r1], None, real_vocab=v_real, nthreads=P.host_threads())
+        st = P.check_fwd(lp_all[r0:r1], ls_all[r0:r1], lo, so, np.ones(r1 - r0, bool),
+                         f"lmhead 4096 tokens {r0}:{r1}")
+        worst = {kk: max(worst[kk], st[kk]) for kk in worst}
+        del z
+    print(worst, flush=True)
     # the 64 tiles grouped into 2, 4 and 8 virtual shards: the same bits
     for s in (2, 4, 8):
         lp_s, lse_s, _ = run(h, w, tgt, None, v_real, v_pad, 64, shards=s)

@@ -11,6 +11,8 @@ The shapes are drawn once from a fixed seed, so the sweep is reproducible.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -42,7 +44,8 @@ def draw_cases(count: int, seed: int):
     return cases
 
 
-CASES = draw_cases(24, seed=20261202)
+# RLK_RANDOM_SHAPES=300 runs the longer stress sweep the design notes quote
+CASES = draw_cases(int(os.environ.get("RLK_RANDOM_SHAPES", "24")), seed=20261202)
 
 
 @pytest.fixture(scope="module")

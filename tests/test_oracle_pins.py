@@ -340,6 +340,11 @@ def pin_lmhead(o):
     z1 = o.lmhead_logits(e, w, real_vocab=v_real)
     for r, col in enumerate((0, 17, k - 1)):
         assert np.array_equal(z1[r], decode(w[:v_real, col]))
+    # the matrix-product form agrees with the plain loops (and so with the decode
+    # through struct above), padding rows unread
+    zb = o.lmhead_logits_blas(h, w, real_vocab=v_real)
+    assert zb.shape == z.shape and np.max(np.abs(zb - z)) <= 1e-12 * max(1.0, np.max(np.abs(z)))
+    assert np.array_equal(o.lmhead_logits_blas(e, w, real_vocab=v_real), z1)
     # the selected-token logp of the fused variant is the log-softmax of z
     tgt = rng.integers(0, v_real, size=n).astype(np.int32)
     lp, ls, _, _ = o.lmhead_fwd(h, w, tgt, real_vocab=v_real)
