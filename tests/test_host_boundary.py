@@ -396,6 +396,22 @@ def test_conveniences_check_tensors_before_anything_runs():
                          torch.zeros(v - 1, 64, dtype=torch.bfloat16), t32, real_vocab=v)
     with pytest.raises(TypeError, match="int32"):
         rlk.selected_token_logprob(x, t32.long(), real_vocab=v, num_vocab_tiles=4)
+    # a view narrower than padded_vocab, or real_vocab beyond it, is refused before any
+    # call: the kernels read columns [0, padded_vocab) of every row
+    wide = torch.zeros(n, 2 * v, dtype=torch.bfloat16)
+    narrow = wide[:, v // 2: v // 2 + v // 2]
+    for call in (lambda **k: rlk.forward(narrow, t32, **k),
+                 lambda **k: rlk.forward_ex(narrow, t32, **k),
+                 lambda **k: rlk.backward(narrow, t32, None, g, g, **k),
+                 lambda **k: rlk.backward_ex(narrow, t32, None, g, None, g, None, None, **k),
+                 lambda **k: rlk.forward_backward(narrow, t32, None, g, **k),
+                 lambda **k: rlk.selected_token_logprob(narrow, t32, **k)):
+        with pytest.raises(ValueError, match="exceeds"):
+            call(real_vocab=v // 2, padded_vocab=v, num_vocab_tiles=4)
+        with pytest.raises(ValueError, match="exceeds"):
+            call(real_vocab=v, num_vocab_tiles=4)  # real_vocab beyond the view's width
+    with pytest.raises(ValueError, match="positive"):
+        rlk.forward(x, t32, real_vocab=0, num_vocab_tiles=4)
 
 
 def test_noalloc_forward_host_validation():

@@ -269,6 +269,22 @@ def _check_inputs(logits, targets, active_mask, **vectors):
     _check_device(logits, targets=targets, active_mask=active_mask, **vectors)
 
 
+def _check_vocab(logits, real_vocab, padded_vocab):
+    """The kernels read columns [0, V_pad) of every row (V_pad = padded_vocab, or the
+    logits' width): a view narrower than that would let them read past it."""
+    import operator
+    _check_logits(logits)
+    v_pad = operator.index(padded_vocab) if padded_vocab else logits.shape[1]
+    if operator.index(real_vocab) < 1:
+        raise ValueError(f"real_vocab must be positive, got {real_vocab!r}")
+    if v_pad > logits.shape[1]:
+        raise ValueError(f"padded_vocab={v_pad} exceeds the {logits.shape[1]} columns of the "
+                         "logits")
+    if real_vocab > v_pad:
+        raise ValueError(f"real_vocab={real_vocab} exceeds padded_vocab={v_pad}")
+    return v_pad
+
+
 def _u8_mask(mask):
     if mask is None:
         return None
@@ -287,6 +303,7 @@ def forward(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *, re
             num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
             workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse), fp32 [N] each.  logits: bf16 [N, ld] with unit column stride."""
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask)
     n = logits.shape[0]
     desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
@@ -307,6 +324,7 @@ def backward(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: torc
     """dlogits [N, V_pad] (fp32 or bf16)."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask, lse=lse, grad_logp=grad_logp)
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
@@ -327,6 +345,7 @@ def forward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask=None, *,
                num_virtual_shards: int = 1, ignore_index: int = -100, validate: bool = False,
                workspace: torch.Tensor | None = None, stream=None):
     """(logp, lse, entropy), fp32 [N] each."""
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask)
     n = logits.shape[0]
     desc = make_desc(n, real_vocab, padded_vocab or logits.shape[1], logits.stride(0),
@@ -353,6 +372,7 @@ def backward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask, lse: t
     """dlogits [N, V_pad] of a loss on (logp, lse, entropy); absent gradients are zero."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask, lse=lse, entropy=entropy, grad_logp=grad_logp,
                   grad_lse=grad_lse, grad_ent=grad_ent)
     n = logits.shape[0]
@@ -416,6 +436,7 @@ def selected_token_logprob(logits: torch.Tensor, targets: torch.Tensor, active_m
     autograd hands the three upstream gradients to rlk_logp_bwd_ex.  logits is
     bf16 [N, ld] with unit column stride; its gradient has its dtype.
     """
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask)
     return _SelectedTokenLogprob.apply(logits, targets, active_mask, real_vocab, padded_vocab,
                                        num_vocab_tiles, ignore_index)
@@ -431,6 +452,7 @@ def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
     if grad_logp is None:
         raise TypeError("grad_logp must be a torch.Tensor")
+    _check_vocab(logits, real_vocab, padded_vocab)
     _check_inputs(logits, targets, active_mask, grad_logp=grad_logp)
     n = logits.shape[0]
     v_pad = padded_vocab or logits.shape[1]
