@@ -40,7 +40,9 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "logits GB/s + tokens/s, fwd+bwd selected-token logp, V=151936; % HBM peak"
 KERNEL_SOURCE = ROOT / "vocab_selected_token_amd" / "csrc" / "rlk_kernels.hip"
+LMHEAD_SOURCE = ROOT / "vocab_selected_token_amd" / "csrc" / "rlk_lmhead.hip"
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_large_32k.txt"
+LMHEAD_TRAFFIC_FILE = ROOT / "profiles" / "traffic_lmhead_4096.txt"
 
 
 def log(*a):
@@ -69,10 +71,10 @@ def algorithmic_bytes_one_pass(wl) -> int:
     return n * wl.real_vocab * 2 + n * wl.padded_vocab * out_b + 17 * n
 
 
-def kernel_source_sha() -> str:
-    """Hash of the kernel source with comments and whitespace removed: it changes
+def kernel_source_sha(source: Path = KERNEL_SOURCE) -> str:
+    """Hash of a kernel source with comments and whitespace removed: it changes
     exactly when the code the counters were taken on changes."""
-    text = KERNEL_SOURCE.read_text()
+    text = source.read_text()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
@@ -104,17 +106,17 @@ def measured_ceilings():
     return out
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+def read_traffic(kernel: str, path: Path = TRAFFIC_FILE, source: Path = KERNEL_SOURCE):
+    """HBM bytes per launch of `kernel` from a committed counter summary, or None
     when the summary is missing or was taken on a different kernel source."""
-    if not TRAFFIC_FILE.exists():
+    if not path.exists():
         return None
     vals = {}
-    for line in TRAFFIC_FILE.read_text().splitlines():
+    for line in path.read_text().splitlines():
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_sha():
+    if vals.get("kernel_source_sha256") != kernel_source_sha(source):
         return None
     key = f"{kernel}_hbm_bytes_per_launch"
     return float(vals[key]) if key in vals else None
@@ -262,6 +264,23 @@ def fingerprints(rlk, wl, inp, mask_u8, shard_counts=(1, 8)) -> dict:
     return out
 
 
+def copy_probe(args, dev) -> None:
+    """A plain copy of known size (untimed), whose FETCH_SIZE / WRITE_SIZE readings
+    scale the counters of the kernels in the same profiled run."""
+    import torch
+
+    if args.copy_probe_gib <= 0:
+        return
+    nbytes = int(args.copy_probe_gib * 2 ** 30)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copy probe {nbytes} bytes x3 done")
+    del src, dst
+
+
 LMHEAD_WORKLOAD = "lmhead_b4096_k4096_v151936_p152576"
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, vendor figure
 
@@ -345,6 +364,7 @@ def bench_lmhead(args) -> int:
         lib_ms = e0.elapsed_time(e1) / args.steps
         library = {"ms": round(lib_ms, 4), "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
                    "note": "torch.matmul bf16 -> bf16 logits (materialised), no logp"}
+    copy_probe(args, dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -360,7 +380,9 @@ def bench_lmhead(args) -> int:
         "tokens_per_s": round(n / (ev_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": read_traffic("lmhead_segments", LMHEAD_TRAFFIC_FILE,
+                                             LMHEAD_SOURCE),
                      "kernel": "lmhead_segments+lmhead_tiles+stage2_merge"},
         "cpu_baseline": cpu,
         "library_gemm": library,
@@ -539,15 +561,7 @@ def main() -> int:
                                                     4)
         log(f"bench: one-launch schedule {ms_one:.3f} ms/step")
 
-    if args.copy_probe_gib > 0:  # plain copy kernel of known size, for counter scaling
-        nbytes = int(args.copy_probe_gib * 2 ** 30)
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"bench: copy probe {nbytes} bytes x3 done")
-        del src, dst
+    copy_probe(args, dev)
 
     shas = None
     if not args.no_sha:

@@ -44,3 +44,13 @@ def test_fp32_dlogits_count_four_bytes():
     assert wl.dlogits_dtype == "f32"
     b = bench.algorithmic_bytes(wl, 0)
     assert b["bwd"] == wl.num_tokens * wl.padded_vocab * 4 + 13 * wl.num_tokens
+
+
+def test_committed_traffic_matches_the_current_kernels():
+    """The counter summaries under profiles/ were taken on the kernel sources as they
+    stand (the bench line reports traffic only while the hashes agree)."""
+    assert bench.read_traffic("bwd_dlogits") is not None
+    assert bench.read_traffic("stage1") is not None
+    assert bench.read_traffic("fwd_bwd_rows") is not None
+    assert bench.read_traffic("lmhead_segments", bench.LMHEAD_TRAFFIC_FILE,
+                              bench.LMHEAD_SOURCE) is not None
