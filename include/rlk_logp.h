@@ -241,10 +241,21 @@ rlk_status rlk_logp_bwd_ex(const rlk_logp_desc* desc, const void* logits, const 
  * per-token weights are fixed in advance).  The outputs are bitwise those of
  * rlk_logp_fwd followed by rlk_logp_bwd on the same arguments -- the same tile
  * partials, the same ascending merge, the same gradient arithmetic -- for every
- * num_virtual_shards; one block owns a row, so the row's second read (for dX)
- * follows its first and is served by the caches: HBM sees one read of the
- * logits and one write of dX instead of two reads and one write.  This
- * single-pass schedule is not on the pages; the contract is [PR289]'s.
+ * num_virtual_shards; HBM sees one read of the logits and one write of dX
+ * instead of two reads and one write.  This single-pass schedule is not on the
+ * pages; the contract is [PR289]'s.
+ *
+ * Two schedules, the same bits:
+ *   - units (T <= 64 tiles of 8 to about 2,500 columns, e.g. 64 tiles over a
+ *     152,576-column row): a block takes 8 consecutive tiles of a row, keeps
+ *     their logits in registers, exchanges its tiles' (max, sumexp) partials
+ *     with the row's other blocks through 64-bit slots in the workspace, and
+ *     writes dX from the registers.  A block waits for its row's slots a
+ *     bounded number of polls (environment variable RLK_FB_SPIN_LIMIT, read
+ *     once per process, default 16384; 0 skips the wait) and past it computes
+ *     the row's partials itself.
+ *   - rows (any other geometry, or a workspace of only the status words): one
+ *     block per row, its second read served by the caches.
  *   desc        as for rlk_logp_fwd, with num_vocab_tiles <= 1024 (the row's
  *               partials live in on-chip memory); num_virtual_shards is
  *               validated and, as everywhere, changes nothing.
@@ -252,8 +263,11 @@ rlk_status rlk_logp_bwd_ex(const rlk_logp_desc* desc, const void* logits, const 
  *   grad_logp   (device) float [N]: g, read on effective-active rows only.
  *   logp, lse   (device) float [N] out, as for rlk_logp_fwd.
  *   dlogits, ld_dlogits, dlogits_dtype  out, as for rlk_logp_bwd.
- *   workspace   >= rlk_logp_fwd_bwd_workspace_bytes(desc) bytes (the 256
- *               bytes of status words), 256-byte aligned.
+ *   workspace   >= 256 bytes (the status words), 256-byte aligned; with
+ *               rlk_logp_fwd_bwd_workspace_bytes(desc) bytes (256 + 8 N T
+ *               where the unit schedule takes the geometry, else 256) the
+ *               unit schedule runs.  Its slots are overwritten on every call:
+ *               calls that share a workspace must not overlap.
  * Errors as for rlk_logp_fwd (RLK_ERR_BAD_TILING also for T > 1024) and
  * rlk_logp_bwd. */
 size_t rlk_logp_fwd_bwd_workspace_bytes(const rlk_logp_desc* desc);

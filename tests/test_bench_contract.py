@@ -51,6 +51,6 @@ def test_committed_traffic_matches_the_current_kernels():
     stand (the bench line reports traffic only while the hashes agree)."""
     assert bench.read_traffic("bwd_dlogits") is not None
     assert bench.read_traffic("stage1") is not None
-    assert bench.read_traffic("fwd_bwd_rows") is not None
+    assert bench.read_traffic("fwd_bwd_units") is not None
     assert bench.read_traffic("lmhead_segments", bench.LMHEAD_TRAFFIC_FILE,
                               bench.LMHEAD_SOURCE) is not None

@@ -7,6 +7,9 @@ here before it reaches a GPU.
 
   * stage 1 (tile_partial): per (lane, slot) the chunk a 16-lane group loads and
     the columns it keeps after masking, for every tile of 310 shapes;
+  * the one-launch forward+backward's unit schedule (fwd_bwd_units): which
+    geometries take it, and that its dX writes cover every column of the row
+    once, for 3,000 shapes;
   * the XCD-local block renumbering: a bijection on every grid size used;
   * the fused LM-head's shard launch loop (lmhead_segments, lmhead_tiles): block
     order, weight rows loaded, segment slots written and the segments each tile
@@ -119,6 +122,99 @@ def test_stage1_model_catches_a_coverage_mistake():
     _, good = stage1_tile(lo, hi)
     _, shifted = stage1_tile(lo + 8, hi)
     assert set(good.tolist()) - set(shifted.tolist())
+
+
+# --------------------------------------------------------------------------
+# the unit schedule of the one-launch forward+backward
+# --------------------------------------------------------------------------
+UNIT_MAX_PASS = 4
+
+
+def fb_desc(real: int, pad: int, tiles: int, n: int = 2):
+    return rlk.make_desc(n, real, pad, (pad + 7) // 8 * 8, tiles, 1, -100, False)
+
+
+def units_fit(real: int, pad: int, tiles: int) -> bool:
+    """The rule fwd_bwd_units_fit states: T <= 64, tiles of at least 8 columns,
+    and every tile's full chunks within 4 passes of one 16-lane group."""
+    if tiles > 64 or pad // tiles < 8:
+        return False
+    bounds, _ = geometry(pad, tiles)
+    for t in range(tiles):
+        lo = int(bounds[t])
+        hi = max(min(int(bounds[t + 1]), real), lo)
+        cf_lo = (lo + 7) >> 3
+        cf_hi = max(hi >> 3, cf_lo)
+        base0 = cf_lo & ~7
+        npass = (cf_hi - base0 + PASS_CHUNKS - 1) // PASS_CHUNKS if cf_hi > cf_lo else 0
+        if npass > UNIT_MAX_PASS:
+            return False
+    return True
+
+
+def units_dx_chunks(real: int, pad: int, tiles: int):
+    """The dX chunks each tile's group writes in fwd_bwd_units: the full chunks of
+    its passes (from registers), lane 1's tail chunk (the chunk cut by the tile's
+    real upper bound, when the tile has one), and zeros for the chunks whose first
+    column lies in the tile's padded bounds at or past V_real."""
+    bounds, _ = geometry(pad, tiles)
+    out = []
+    for t in range(tiles):
+        plo, phi = int(bounds[t]), int(bounds[t + 1])
+        lo = plo
+        hi = max(min(phi, real), lo)
+        cf_lo = (lo + 7) >> 3
+        cf_hi = max(hi >> 3, cf_lo)
+        out.extend(range(cf_lo, cf_hi))
+        if hi > lo and (hi & 7) and (hi >> 3) >= cf_lo:
+            out.append(hi >> 3)
+        out.extend(range(max((plo + 7) >> 3, (real + 7) >> 3), (phi + 7) >> 3))
+    return np.array(out, dtype=np.int64)
+
+
+def unit_shapes():
+    rng = random.Random(20261204)
+    shapes = [(151936, 152576, 64), (151936, 151936, 64), (151936, 152584, 64),
+              (8, 8, 1), (63, 64, 8), (64, 64, 8), (65, 72, 9), (2504, 2504, 1),
+              (2505, 2512, 1), (5000, 5120, 64), (3001, 3008, 5), (12345, 12352, 7),
+              (60, 63, 9), (7, 7, 1), (500, 512, 65)]
+    while len(shapes) < 3000:
+        tiles = rng.randint(1, rng.choice([4, 64, 80]))
+        width = rng.choice([8, 9, 15, 16, rng.randint(8, 64), rng.randint(8, 2600)])
+        pad = tiles * width + rng.randint(0, tiles - 1)
+        real = max(1, pad - rng.choice([0, 0, 1, 7, 8, 9, rng.randint(0, 3 * width)]))
+        shapes.append((real, pad, tiles))
+    return shapes
+
+
+def test_unit_schedule_writes_every_dx_column_once():
+    taken = 0
+    for real, pad, tiles in unit_shapes():
+        fits = units_fit(real, pad, tiles)
+        ws = rlk.rlk_logp_fwd_bwd_workspace_bytes(fb_desc(real, pad, tiles, n=3))
+        # the library takes the unit schedule exactly where the rule says
+        assert ws == (256 + 3 * tiles * 8 if fits else 256), (real, pad, tiles)
+        if not fits:
+            continue
+        taken += 1
+        chunks = units_dx_chunks(real, pad, tiles)
+        count = np.bincount(chunks, minlength=(pad + 7) // 8)
+        assert count.size == (pad + 7) // 8, (real, pad, tiles)  # nothing past the row
+        assert (count == 1).all(), (real, pad, tiles, np.flatnonzero(count != 1)[:8])
+    assert taken > 2000
+
+
+def test_unit_model_catches_a_double_write():
+    """The model itself: without the tail-chunk rule a tile bound that is not a
+    multiple of 8 leaves its chunk unwritten; with the head chunk written as well
+    it is written twice."""
+    real, pad, tiles = 3001, 3008, 5  # bounds at 601, 1203, ...: not multiples of 8
+    chunks = units_dx_chunks(real, pad, tiles)
+    assert (np.bincount(chunks) == 1).all()
+    bounds, _ = geometry(pad, tiles)
+    heads = [int(b) >> 3 for b in bounds[1:-1] if int(b) & 7]
+    assert heads
+    assert (np.bincount(np.concatenate([chunks, heads])) == 2).any()
 
 
 # --------------------------------------------------------------------------

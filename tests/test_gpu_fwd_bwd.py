@@ -165,6 +165,68 @@ def test_larger_batches_parity_and_bitwise_equality(orc, case):
                                                                       bits(b)[~na]), f"S={s} {name}"
 
 
+# Geometries the unit schedule takes (T <= 64, tiles of 8 to about 2,500
+# columns): full-size tiles of four passes, tile bounds off the 8-column grid,
+# a last unit with fewer than 4 tiles, 8- and 9-column tiles, a real vocabulary
+# ending inside a chunk, whole tiles of padding, one tile per row.
+UNIT_SHAPES = [
+    dict(n=300, real=151936, pad=152576, T=64),
+    dict(n=64, real=5000, pad=5120, ld=5128, T=64),
+    dict(n=9, real=3001, pad=3008, T=5, spike=True),
+    dict(n=33, real=2374 * 3 + 1, pad=2374 * 3 + 8, T=3),
+    dict(n=40, real=500, pad=512, T=64),
+    dict(n=40, real=515, pad=600, T=64),
+    dict(n=20, real=700, pad=2048, T=64),
+    dict(n=17, real=1, pad=8, T=1),
+    dict(n=50, real=2504, pad=2504, T=1),
+    dict(n=1100, real=9000, pad=9001, T=61),
+]
+
+
+def rows_schedule(inp, dtype):
+    """forward_backward with only the status words as workspace: one block per row."""
+    wl = inp.wl
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    return rlk.forward_backward(inp.logits, inp.targets, inp.mask, inp.grad,
+                                real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                                num_vocab_tiles=wl.num_tiles, out_dtype=dtype, workspace=ws)
+
+
+def assert_same_bits_nan(a3, b3, what):
+    for a, b, name in zip(a3, b3, ("logp", "lse", "dlogits")):
+        na, nb = torch.isnan(a), torch.isnan(b)
+        assert torch.equal(na, nb), f"{what} {name}: NaN pattern differs"
+        assert torch.equal(bits(a)[~na], bits(b)[~nb]), f"{what} {name}: bits differ"
+
+
+@pytest.mark.parametrize("case", UNIT_SHAPES,
+                         ids=lambda c: f"n{c['n']}_v{c['real']}_p{c['pad']}_T{c['T']}")
+def test_unit_schedule_matches_row_schedule(case):
+    """Where the geometry fits, rlk_logp_fwd_bwd with its full workspace runs the
+    unit schedule (blocks of 4 tiles that exchange partials); with only the
+    status words it runs one block per row.  Both give the bits of the separate
+    calls, on rows with NaN, +inf and no finite logit too."""
+    print(f"case {case}", flush=True)
+    wl = W.small_workload(case["n"], case["real"], case["pad"], ld=case.get("ld"),
+                          num_tiles=case["T"], spike_frac=0.3 if case.get("spike") else 0.0,
+                          spike=12.0, seed=case["n"] + 5000)
+    d = rlk.make_desc(wl.num_tokens, wl.real_vocab, wl.padded_vocab, wl.ld_logits, wl.num_tiles)
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(d) == 256 + 8 * wl.num_tokens * wl.num_tiles
+    inp = W.make_inputs(wl, DEV)
+    n = wl.num_tokens
+    if n > 6:
+        inp.logits[1, :wl.real_vocab] = float("-inf")
+        inp.logits[2, wl.real_vocab - 1] = float("nan")
+        inp.logits[3, 0] = float("inf")
+        inp.mask[1] = True
+        inp.targets[4] = wl.real_vocab + 3  # a bad target on an active row
+        inp.mask[4] = True
+    for dt in (torch.float32, torch.bfloat16):
+        units = fused(inp, dt)
+        assert_same_bits_nan(units, rows_schedule(inp, dt), f"{case} {dt} units vs rows")
+        assert_same_bits_nan(units, separate(inp, dt), f"{case} {dt} units vs separate")
+
+
 def test_empty_batch():
     wl = W.small_workload(0, 100)
     inp = W.make_inputs(wl, DEV)

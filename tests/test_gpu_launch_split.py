@@ -52,6 +52,25 @@ def test_split_launches_give_the_same_bits(tmp_path):
                 assert torch.equal(a, b), f"{key} differs with a {limit}-thread launch limit"
 
 
+def test_unit_schedule_fallback_gives_the_same_bits(tmp_path):
+    """The one-launch unit schedule bounds each block's wait for the other units
+    of its row; past the bound the block computes the row's partials itself.
+    RLK_FB_SPIN_LIMIT=0 (read once per process) sends every block down that path
+    at once: a child process runs the same case and its bits must equal this
+    process's, which waits for the published partials."""
+    ref = run_all(*make_case())
+    out = tmp_path / "bits_fallback.pt"
+    env = dict(os.environ, RLK_FB_SPIN_LIMIT="0")
+    print("spin limit 0 (child process)", flush=True)
+    r = subprocess.run([sys.executable, "-u", "-m", "tests.split_child", str(out)], cwd=ROOT,
+                       env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, f"child failed:\n{r.stdout[-2000:]}\n{r.stderr[-3000:]}"
+    got = torch.load(out, weights_only=True)
+    for key in ref:
+        for a, b in zip(ref[key], got[key]):
+            assert torch.equal(a, b), f"{key} differs when every block computes its row itself"
+
+
 def test_backward_split_at_full_size():
     """The split without the override: 224,000 rows of 152576 columns (68 GB of bf16
     logits, and as much bf16 dX) put the backward at 224,000 x 75 blocks of 128

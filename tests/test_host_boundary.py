@@ -252,8 +252,14 @@ def test_fwd_bwd_host_validation():
     a = _FakeTensor(0x10000000)
     s = _NoStream()
     ok = desc(num_tokens=8, num_vocab_tiles=64)
-    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(ok) == 256
+    # the status words, plus one 64-bit partial slot per (row, tile) where the
+    # unit schedule takes the geometry (T <= 64 tiles of 8 to about 2,500 columns)
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(ok) == 256 + 8 * 64 * 8
     assert rlk.rlk_logp_fwd_bwd_workspace_bytes(desc(num_vocab_tiles=1024)) == 256
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(desc(num_tokens=8, num_vocab_tiles=1)) == 256 + 64
+    wide = desc(num_tokens=8, real_vocab=4000, padded_vocab=4096, ld_logits=4096,
+                num_vocab_tiles=1)  # one 4096-column tile: 7 passes
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(wide) == 256
     # the row's partials live on chip: at most 1024 tiles
     big = desc(num_tokens=8, real_vocab=4000, padded_vocab=4096, ld_logits=4096,
                num_vocab_tiles=1025)

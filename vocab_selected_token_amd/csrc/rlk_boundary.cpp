@@ -391,9 +391,22 @@ rlk_status check_fwd_bwd_desc(const rlk_logp_desc* d) {
 
 }  // namespace
 
+namespace {
+
+// Bytes of partial slots the unit schedule needs for desc (0 where it does not
+// apply: the one-block-per-row schedule runs with the status words alone).
+size_t fwd_bwd_slot_bytes(const rlk_logp_desc* d) {
+  if (!rlk::fwd_bwd_units_fit((int32_t)d->real_vocab, (int32_t)d->padded_vocab,
+                              d->num_vocab_tiles))
+    return 0;
+  return (size_t)d->num_tokens * (size_t)d->num_vocab_tiles * sizeof(uint64_t);
+}
+
+}  // namespace
+
 size_t rlk_logp_fwd_bwd_workspace_bytes(const rlk_logp_desc* desc) {
   if (check_fwd_bwd_desc(desc) != RLK_OK) return 0;
-  return kStatusBytes;
+  return kStatusBytes + fwd_bwd_slot_bytes(desc);
 }
 
 rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
@@ -453,8 +466,13 @@ rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
   a.ld_d = ld_dlogits;
   a.out_bf16 = dlogits_dtype == RLK_DTYPE_BF16;
   a.status = status;
+  // the unit schedule where the geometry fits and the workspace holds its slots
+  const size_t slot_bytes = fwd_bwd_slot_bytes(desc);
+  a.slots = (slot_bytes > 0 && workspace_bytes >= kStatusBytes + slot_bytes)
+                ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kStatusBytes)
+                : nullptr;
   e = rlk::launch_fwd_bwd(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "fwd_bwd_rows launch");
+  if (e != hipSuccess) return hip_fail(e, "fwd_bwd launch");
   if (validate) return finish_validate(status, stream, true);
   return ok();
 }
@@ -631,12 +649,28 @@ int64_t read_thread_limit() {
   return n < kLimit ? (int64_t)n : kLimit;
 }
 
+int32_t read_spin_limit() {
+  constexpr int32_t kDefault = 1 << 14;
+  const char* v = getenv("RLK_FB_SPIN_LIMIT");
+  if (!v || !*v) return kDefault;
+  char* end = nullptr;
+  const long long n = strtoll(v, &end, 10);
+  if (end == v) return kDefault;
+  if (n < 0) return 0;
+  return n < (1 << 30) ? (int32_t)n : (1 << 30);
+}
+
 }  // namespace
 
 // The environment is read once, at the first launch of the process (a
 // function-local static: initialised once, safely under concurrent first calls).
 int64_t launch_thread_limit() {
   static const int64_t limit = read_thread_limit();
+  return limit;
+}
+
+int32_t fwd_bwd_spin_limit() {
+  static const int32_t limit = read_spin_limit();
   return limit;
 }
 

@@ -84,7 +84,19 @@ struct FwdBwdArgs {
   int64_t ld_d;
   bool out_bf16;
   uint32_t* status;
+  // Unit schedule: [num_rows][num_tiles] 64-bit partial slots, or null for the
+  // one-block-per-row schedule (the same bits either way).
+  uint64_t* slots;
 };
+
+// Whether the unit schedule of the one-launch forward+backward takes this
+// geometry: T <= 64, tiles of at least 8 columns, and every tile's full
+// chunks within the passes a lane group keeps in registers.
+bool fwd_bwd_units_fit(int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles);
+// Polls of a row's partial slots before a block computes them itself (read
+// once per process: RLK_FB_SPIN_LIMIT, default 16384; 0 makes every block
+// compute its row's partials itself -- a hook for tests).
+int32_t fwd_bwd_spin_limit();
 
 // Fused LM-head variant: vocabulary rows per GEMM block (tiles must be at
 // least this wide, so a block holds at most one tile bound).

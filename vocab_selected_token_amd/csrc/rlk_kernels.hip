@@ -188,6 +188,55 @@ __device__ __forceinline__ void fold_pass(const uint4 (&q)[kChunks], int32_t b, 
   fold_values<kChunks * 8, kEnt>(v, m, s, a);
 }
 
+// The chunk cut by a tile bound, masked to the columns [e_lo, e_hi) that
+// belong to the tile, folded into (m, s, a).
+template <bool kEnt>
+__device__ __forceinline__ void fold_edge(const uint4& qe, int32_t e_lo, int32_t e_hi, float& m,
+                                          float& s, float& a) {
+  float v[8];
+  unpack8(qe, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < e_lo || e >= e_hi) v[e] = kNegInf;
+  fold_values<8, kEnt>(v, m, s, a);
+}
+
+// The 16 lanes of a group combined: an exact max, then each lane's sums
+// rescaled to it and added over a fixed rotate tree; (-inf, 0) (and la = 0)
+// when the whole tile is -inf.  Every lane of the group returns the result.
+template <bool kEnt>
+__device__ __forceinline__ void group_reduce(float m, float s, float a, float& gm_out,
+                                             float& ls_out, float& la_out) {
+  float gm = m;
+  gm = maxnan(gm, row_ror<8>(gm));
+  gm = maxnan(gm, row_ror<4>(gm));
+  gm = maxnan(gm, row_ror<2>(gm));
+  gm = maxnan(gm, row_ror<1>(gm));
+  float ls = 0.0f, la = 0.0f;
+  if (gm != kNegInf && m != kNegInf) {
+    const float r = exp2_hw((m - gm) * kLog2e);
+    ls = s * r;
+    if (kEnt) la = (a + (m - gm) * s) * r;
+  }
+  ls += row_ror<8>(ls);
+  ls += row_ror<4>(ls);
+  ls += row_ror<2>(ls);
+  ls += row_ror<1>(ls);
+  if (kEnt) {
+    la += row_ror<8>(la);
+    la += row_ror<4>(la);
+    la += row_ror<2>(la);
+    la += row_ror<1>(la);
+  }
+  if (gm == kNegInf) {  // the (-inf, 0) identity partial
+    ls = 0.0f;
+    la = 0.0f;
+  }
+  gm_out = gm;
+  ls_out = ls;
+  la_out = la;
+}
+
 // Columns [lo, hi) of tile `tile`: floor(t * V_pad / T) bounds (tile_width =
 // V_pad / T when T divides V_pad, else 0), cut at V_real so that padded
 // columns never count; an all-padding tile is empty.
@@ -254,14 +303,7 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
     if (npass > 1) load_pass<kNt>(qb, rowp, base0 + kPassChunks, cf_lo, cf_hi, gl);
   }
   if (kDepth == 3 && npass > 2) load_pass<kNt>(qc, rowp, base0 + 2 * kPassChunks, cf_lo, cf_hi, gl);
-  if (c >= 0) {
-    float v[8];
-    unpack8(qe, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e < e_lo || e >= e_hi) v[e] = kNegInf;
-    fold_values<8, kEnt>(v, m, s, a);
-  }
+  if (c >= 0) fold_edge<kEnt>(qe, e_lo, e_hi, m, s, a);
   if (kDepth == 1) {
     for (int32_t p = 0; p < npass; ++p) {
       const int32_t b = base0 + p * kPassChunks;
@@ -293,34 +335,7 @@ __device__ __forceinline__ void tile_partial(const uint4* __restrict__ rowp, int
     }
   }
 
-  float gm = m;
-  gm = maxnan(gm, row_ror<8>(gm));
-  gm = maxnan(gm, row_ror<4>(gm));
-  gm = maxnan(gm, row_ror<2>(gm));
-  gm = maxnan(gm, row_ror<1>(gm));
-  float ls = 0.0f, la = 0.0f;
-  if (gm != kNegInf && m != kNegInf) {
-    const float r = exp2_hw((m - gm) * kLog2e);
-    ls = s * r;
-    if (kEnt) la = (a + (m - gm) * s) * r;
-  }
-  ls += row_ror<8>(ls);
-  ls += row_ror<4>(ls);
-  ls += row_ror<2>(ls);
-  ls += row_ror<1>(ls);
-  if (kEnt) {
-    la += row_ror<8>(la);
-    la += row_ror<4>(la);
-    la += row_ror<2>(la);
-    la += row_ror<1>(la);
-  }
-  if (gm == kNegInf) {  // the (-inf, 0) identity partial
-    ls = 0.0f;
-    la = 0.0f;
-  }
-  gm_out = gm;
-  ls_out = ls;
-  la_out = la;
+  group_reduce<kEnt>(m, s, a, gm_out, ls_out, la_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1068,6 +1083,294 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward and backward in one launch, split across blocks: one block owns a
+// unit of kUnitWaves * 4 consecutive tiles of one row and keeps them in
+// registers from the read to the dX write, so HBM sees exactly one read of the
+// logits and one write of dX.
+//   1. each 16-lane group reduces its tile with the stage-1 code (lane
+//      mapping, fold order and rotate tree of tile_partial), holding every
+//      chunk it loads;
+//   2. the group publishes the tile's (max, sumexp) pair as one 64-bit relaxed
+//      atomic store at agent scope into the row's slot for that tile, which a
+//      fill kernel has set to kSlotEmpty;
+//   3. wave 0 polls the row's T <= 64 slots (one per lane, relaxed atomic
+//      loads at agent scope) until none is empty, then merges them with the
+//      stage-2 arithmetic;
+//   4. the block writes dX of its columns from the registers.
+// A pair is a single 64-bit access, so a reader sees either the sentinel or
+// both halves of the partial: no fence is needed between the data and a flag
+// (a device-scope release would write back the L2 full of dX lines), only the
+// per-location coherence that relaxed atomics have across the XCDs.  The
+// sentinel is not a pair the reduction can produce: its max half would be a NaN
+// whose low 16 bits are set, and a tile max is an input logit (a bf16 value
+// widened, low 16 bits zero), -inf or the hardware's default NaN.
+//
+// Progress: a block waits only for the other units of its row, which are the
+// neighbouring block indices.  The poll is bounded: after spin_limit polls
+// (or at once when spin_limit <= 0) the block computes all T partials of the
+// row itself, with the same code, and goes on -- the same bits whatever the
+// schedule, and no block waits for ever.
+//
+// Every value is computed by the code of stage1_partials, stage2_merge_waves
+// and bwd_dlogits in the same order, so the outputs are bitwise those of the
+// separate launches.  Each dX chunk has one writer: the tile that holds the
+// chunk's first column (a full chunk in its passes, or its tail chunk, which
+// may reach into the next tile or the padding); chunks that start at or past
+// V_real are zeros written by the tile whose padded bounds hold their first
+// column.  That needs tiles of at least 8 columns (the launcher checks it).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kSlotEmpty = ~0ull;
+constexpr int kUnitMaxPass = 4;  // tiles of up to 4 passes (80 chunks each) per lane group
+constexpr int kUnitWaves = 2;    // waves per block: 8 tiles per unit
+
+// The chunks one lane holds for its tile: slot (p, k) is chunk
+// base0 + p * kPassChunks + k * 16 + gl, plus the chunk cut by a tile bound
+// (lane 0: the head chunk, lane 1: the tail chunk) in qe.
+template <int kMaxPass>
+struct TileRegs {
+  uint4 q[kMaxPass][kChunks];
+  uint4 qe;
+  int32_t c_tail;  // this lane's tail chunk (its dX is written here), or -1
+  int32_t base0, cf_lo, cf_hi, npass;
+};
+
+// tile_partial's loads and arithmetic with every pass loaded up front and kept
+// (npass <= kMaxPass); the same fold order -- the cut chunk, then the passes in
+// ascending order -- and the same group reduction, so the same bits.
+template <int kMaxPass>
+__device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp, int32_t lo,
+                                                  int32_t hi, int gl, TileRegs<kMaxPass>& r,
+                                                  float& gm_out, float& ls_out) {
+  float m = kNegInf, s = 0.0f, a = 0.0f;
+  r.cf_lo = (lo + 7) >> 3;
+  r.cf_hi = hi >> 3;
+  if (r.cf_hi < r.cf_lo) r.cf_hi = r.cf_lo;
+  r.base0 = r.cf_lo & ~7;
+  r.npass = r.cf_hi > r.cf_lo ? (r.cf_hi - r.base0 + kPassChunks - 1) / kPassChunks : 0;
+  int32_t c = -1, e_lo = 0, e_hi = 0;
+  r.c_tail = -1;
+  if (gl == 0 && hi > lo && (lo & 7)) {
+    c = lo >> 3;
+    e_lo = lo & 7;
+    e_hi = min(hi - (c << 3), 8);
+  } else if (gl == 1 && hi > lo && (hi & 7) && (hi >> 3) >= r.cf_lo) {
+    c = hi >> 3;
+    e_lo = 0;
+    e_hi = hi & 7;
+    r.c_tail = c;
+  }
+  if (c >= 0) r.qe = load_stream(rowp + c);
+#pragma unroll
+  for (int p = 0; p < kMaxPass; ++p)
+    if (p < r.npass) load_pass<true>(r.q[p], rowp, r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl);
+  if (c >= 0) fold_edge<false>(r.qe, e_lo, e_hi, m, s, a);
+#pragma unroll
+  for (int p = 0; p < kMaxPass; ++p)
+    if (p < r.npass)
+      fold_pass<false>(r.q[p], r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
+  float la;
+  group_reduce<false>(m, s, a, gm_out, ls_out, la);
+}
+
+// dX of 8 columns at out; n = columns to write (1..8).  bf16: one 16-byte
+// nontemporal store.  fp32: two 16-byte stores; a lane's 32 bytes sit between
+// its neighbours', so each store instruction covers every other 16 bytes of
+// its span, and without the nontemporal hint the L2 joins the two halves of
+// each line (32K rows: 5.46 against 5.80 ms with the hint).
+template <typename OutT>
+__device__ __forceinline__ void store_chunk(OutT* out, const float (&d)[8], int n) {
+  if constexpr (sizeof(OutT) == 2) {
+    Store8<uint16_t>::store(out, d, n);
+  } else if (n == 8) {
+    *reinterpret_cast<u32x4*>(out) = u32x4{__float_as_uint(d[0]), __float_as_uint(d[1]),
+                                           __float_as_uint(d[2]), __float_as_uint(d[3])};
+    *reinterpret_cast<u32x4*>(out + 4) = u32x4{__float_as_uint(d[4]), __float_as_uint(d[5]),
+                                               __float_as_uint(d[6]), __float_as_uint(d[7])};
+  } else {
+    for (int e = 0; e < n; ++e) out[e] = d[e];
+  }
+}
+
+// dX of the tile's chunks from the registers.  A full chunk lies inside the
+// real columns, so dlogits_chunk reduces to one of three forms, chosen once per
+// row (act and bad are the same for the whole block): +0 on an inactive row,
+// NaN on a row with a bad target, else -g exp(x - L) per column with the
+// target's column g (1 - exp(x_t - L)) -- dlogits_chunk's arithmetic.  The
+// tail chunk, which may reach past V_real, takes dlogits_chunk itself.
+template <int kMaxPass, typename OutT>
+__device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass>& r, int gl,
+                                             OutT* __restrict__ orow, bool act, bool bad, float L,
+                                             float g, int32_t tgt, int32_t real_vocab,
+                                             int32_t padded_vocab) {
+  const float ng = -g;
+#pragma unroll
+  for (int p = 0; p < kMaxPass; ++p) {
+    if (p >= r.npass) break;
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int32_t c = r.base0 + p * kPassChunks + k * kGroupLanes + gl;
+      if (c < r.cf_lo || c >= r.cf_hi) continue;
+      const int32_t j0 = c << 3;
+      float d[8];
+      if (act && !bad) {
+        float x[8];
+        unpack8(r.q[p][k], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
+        if (tgt >= j0 && tgt < j0 + 8) {
+          const int e = tgt - j0;
+          d[e] = g * (1.0f - exp2_hw((x[e] - L) * kLog2e));
+        }
+      } else {
+        const float v = act ? __builtin_nanf("") : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = v;
+      }
+      store_chunk<OutT>(orow + j0, d, 8);
+    }
+  }
+  if (r.c_tail >= 0) {
+    const int32_t j0 = r.c_tail << 3;
+    float d[8];
+    dlogits_chunk(r.qe, j0, act, bad, L, g, tgt, real_vocab, d);
+    store_chunk<OutT>(orow + j0, d, min(8, padded_vocab - j0));
+  }
+}
+
+__device__ __forceinline__ uint64_t pack_partial(float m, float s) {
+  return ((uint64_t)__float_as_uint(s) << 32) | __float_as_uint(m);
+}
+
+__global__ __launch_bounds__(256) void fill_slots(uint64_t* __restrict__ slots, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    slots[i] = kSlotEmpty;
+}
+
+template <typename OutT, int kMaxPass, int kUnitWaves>
+__global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
+    const uint4* __restrict__ logits, int64_t ld_chunks, int32_t real_vocab,
+    int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t units_per_row,
+    const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
+    const float* __restrict__ grad, float* __restrict__ logp, float* __restrict__ lse,
+    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status,
+    uint64_t* __restrict__ slots, int32_t spin_limit, int64_t unit_begin) {
+  constexpr int kGroups = kUnitWaves * kGroupsPerWave;  // tiles per unit
+  __shared__ float s_m[64];
+  __shared__ float s_s[64];
+  __shared__ __align__(16) float s_e[64];
+  __shared__ __align__(16) float s_sv[64];
+  __shared__ float s_lse;
+  __shared__ int s_fallback;
+  const int64_t u = unit_begin + blockIdx.x;
+  const int32_t row = (int32_t)(u / units_per_row);
+  const int32_t unit = (int32_t)(u - (int64_t)row * units_per_row);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave * kGroupsPerWave + (lane >> 4);
+  const int gl = lane & 15;
+  const int32_t tile = unit * kGroups + grp;
+  const uint4* __restrict__ rowp = logits + (int64_t)row * ld_chunks;
+
+  // row values, the same in every lane (kept in scalar registers)
+  const bool act_mask = (mask == nullptr || mask[row] != 0);
+  const int32_t tgt = __builtin_amdgcn_readfirstlane(act_mask ? targets[row] : 0);
+  const bool act = __builtin_amdgcn_readfirstlane(act_mask && tgt != ignore_index);
+  const bool bad = act && (tgt < 0 || tgt >= real_vocab);
+  float x_t = 0.0f;
+  if (unit == 0 && threadIdx.x == 0 && act && !bad)
+    x_t = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rowp)[tgt] << 16);
+  const float g = act ? grad[row] : 0.0f;
+
+  // 1. this unit's tiles, kept in registers
+  int32_t lo = 0, hi = 0;
+  if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
+  TileRegs<kMaxPass> tr;
+  float gm, ls;
+  tile_partial_regs<kMaxPass>(rowp, lo, hi, gl, tr, gm, ls);
+  uint64_t* __restrict__ rs = slots + (int64_t)row * num_tiles;
+  // 2. publish
+  if (tile < num_tiles && gl == 0)
+    __hip_atomic_store(rs + tile, pack_partial(gm, ls), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 3. the row's partials, merged in ascending tile order (wave 0)
+  if (wave == 0) {
+    bool ok = false;
+    uint64_t v = kSlotEmpty;
+    for (int32_t it = 0; it < spin_limit; ++it) {
+      if (lane < num_tiles)
+        v = __hip_atomic_load(rs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(lane >= num_tiles || v != kSlotEmpty)) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ok) {
+      const float mt = lane < num_tiles ? __uint_as_float((uint32_t)v) : kNegInf;
+      const float st = lane < num_tiles ? __uint_as_float((uint32_t)(v >> 32)) : 0.0f;
+      const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
+      if (lane == 0) s_lse = L;
+    }
+    if (lane == 0) s_fallback = ok ? 0 : 1;
+  }
+  __syncthreads();
+  if (s_fallback) {
+    // the row's T partials from the logits, by this block alone
+    for (int32_t t0 = 0; t0 < num_tiles; t0 += kGroups) {
+      const int32_t t = t0 + grp;
+      int32_t flo = 0, fhi = 0;
+      if (t < num_tiles) tile_range(t, tile_width, padded_vocab, num_tiles, real_vocab, flo, fhi);
+      float fm, fs, fa;
+      tile_partial<true, 1>(rowp, flo, fhi, gl, fm, fs, fa);
+      if (t < num_tiles && gl == 0) {
+        s_m[t] = fm;
+        s_s[t] = fs;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const float mt = lane < num_tiles ? s_m[lane] : kNegInf;
+      const float st = lane < num_tiles ? s_s[lane] : 0.0f;
+      const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
+      if (lane == 0) s_lse = L;
+    }
+    __syncthreads();
+  }
+  const float Lrow = s_lse;
+  if (unit == 0 && threadIdx.x == 0) {
+    lse[row] = Lrow;
+    if (!act) {
+      logp[row] = 0.0f;
+    } else if (bad) {
+      logp[row] = __builtin_nanf("");
+      status[0] = 1u;
+    } else {
+      logp[row] = x_t - Lrow;
+      if (!__builtin_isfinite(Lrow)) status[1] = 1u;
+    }
+  }
+
+  // 4. dX of this unit's columns
+  if (tile >= num_tiles) return;
+  const float L = act ? Lrow : 0.0f;
+  OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
+  tile_dx_regs<kMaxPass, OutT>(tr, gl, orow, act, bad, L, g, tgt, real_vocab, padded_vocab);
+  // chunks that start at or past V_real inside this tile's padded bounds: +0
+  int32_t plo, phi;
+  if (tile_width) {
+    plo = tile * tile_width;
+    phi = plo + tile_width;
+  } else {
+    plo = (int32_t)(((int64_t)tile * padded_vocab) / num_tiles);
+    phi = (int32_t)(((int64_t)(tile + 1) * padded_vocab) / num_tiles);
+  }
+  const int32_t z_end = (phi + 7) >> 3;
+  const float zero[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int32_t c = max((plo + 7) >> 3, (real_vocab + 7) >> 3) + gl; c < z_end; c += kGroupLanes)
+    store_chunk<OutT>(orow + (c << 3), zero, min(8, padded_vocab - (c << 3)));
+}
+
 __global__ void clear_status(uint32_t* status) {
   if (threadIdx.x < 2) status[threadIdx.x] = 0u;
 }
@@ -1190,8 +1493,61 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
+bool fwd_bwd_units_fit(int32_t real_vocab, int32_t padded_vocab, int32_t num_tiles) {
+  if (num_tiles < 1 || num_tiles > 64 || padded_vocab / num_tiles < 8) return false;
+  // the passes tile_partial_regs takes for each tile (its geometry, on the host)
+  for (int32_t t = 0; t < num_tiles; ++t) {
+    const int64_t lo = (int64_t)t * padded_vocab / num_tiles;
+    int64_t hi = (int64_t)(t + 1) * padded_vocab / num_tiles;
+    if (hi > real_vocab) hi = real_vocab;
+    if (hi < lo) hi = lo;
+    const int64_t cf_lo = (lo + 7) >> 3;
+    int64_t cf_hi = hi >> 3;
+    if (cf_hi < cf_lo) cf_hi = cf_lo;
+    const int64_t base0 = cf_lo & ~int64_t{7};
+    const int64_t npass = cf_hi > cf_lo ? (cf_hi - base0 + kPassChunks - 1) / kPassChunks : 0;
+    if (npass > kUnitMaxPass) return false;
+  }
+  return true;
+}
+
+namespace {
+
+template <typename OutT>
+hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
+  constexpr int kGroups = kUnitWaves * kGroupsPerWave;
+  const int64_t n_slots = (int64_t)a.num_rows * a.num_tiles;
+  const int64_t fill_blocks = (n_slots + 255) / 256 < 8192 ? (n_slots + 255) / 256 : 8192;
+  hipLaunchKernelGGL(fill_slots, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.slots,
+                     n_slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // whole rows per launch: a row's units wait only for each other
+  const int32_t upr = (a.num_tiles + kGroups - 1) / kGroups;
+  const int64_t rows_per_launch = launch_thread_limit() / (kUnitWaves * 64) / upr;
+  const int32_t spin = fwd_bwd_spin_limit();
+  const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
+    const int64_t nr = a.num_rows - r0 < rows_per_launch ? a.num_rows - r0 : rows_per_launch;
+    hipLaunchKernelGGL((fwd_bwd_units<OutT, kUnitMaxPass, kUnitWaves>), dim3((unsigned)(nr * upr)),
+                       dim3(kUnitWaves * 64), 0, stream, x, a.ld / 8, a.real_vocab,
+                       a.padded_vocab, a.num_tiles, a.tile_width, upr, a.targets, a.mask,
+                       a.ignore_index, a.grad, a.logp, a.lse, dl, a.ld_d, a.status, a.slots, spin,
+                       r0 * upr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_fwd_bwd(const FwdBwdArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
+  if (a.slots) {
+    if (a.out_bf16) return launch_units(a, reinterpret_cast<uint16_t*>(a.dlogits), stream);
+    return launch_units(a, reinterpret_cast<float*>(a.dlogits), stream);
+  }
   const int64_t rows_per_launch = launch_thread_limit() / kFbThreads;
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
   for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
