@@ -122,6 +122,18 @@ def read_traffic(kernel: str, path: Path = TRAFFIC_FILE, source: Path = KERNEL_S
     return float(vals[key]) if key in vals else None
 
 
+def unit_fallbacks(ws, kernel: str):
+    """Blocks of the last unit-schedule call that computed their row's partials
+    themselves instead of receiving them (status word 2 of the workspace); None
+    for the row schedule."""
+    import torch
+
+    if kernel != "fwd_bwd_units":
+        return None
+    torch.cuda.synchronize()
+    return int(ws[:12].view(torch.int32)[2].item())
+
+
 def host_cpu() -> dict:
     """The host the oracle runs on: the cores this process may use (its affinity
     mask), the OMP_NUM_THREADS share a shared machine grants one job, the logical
@@ -548,6 +560,7 @@ def main() -> int:
             step_one(i)
         torch.cuda.synchronize()
         ms_one = (time.perf_counter() - t0) * 1e3 / args.steps
+        fallbacks = unit_fallbacks(ws, one_kernel)
         b_one = algorithmic_bytes_one_pass(wl)
         one_read = {"bytes_per_step": b_one,
                     "two_calls_GB/s": round(b_one / (ms_step * 1e-3) / 1e9, 1),
@@ -556,7 +569,8 @@ def main() -> int:
                     "one_launch_GB/s": round(b_one / (ms_one * 1e-3) / 1e9, 1),
                     "one_launch_hbm_frac": round(b_one / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "one_launch_tokens_per_s": round(n / (ms_one * 1e-3), 1),
-                    "one_launch_kernel": one_kernel}
+                    "one_launch_kernel": one_kernel,
+                    "one_launch_fallback_blocks": fallbacks}
         if ceilings is not None and "row_copy_GBps" in ceilings:
             # what a copy of the same bytes takes on this GPU in the two shapes such a
             # schedule can have, with no arithmetic at all (rlk_calib)
@@ -580,7 +594,8 @@ def main() -> int:
         value = total_bytes / (ms_step * 1e-3) / 1e9
         k_gbs = total_bytes / (fwd_ms * 1e-3) / 1e9
         kernels = {one_kernel: {"ms": round(fwd_ms, 4), "GB/s": round(k_gbs, 1),
-                                "bytes": total_bytes}}
+                                "bytes": total_bytes,
+                                "fallback_blocks": unit_fallbacks(ws, one_kernel)}}
         roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic(one_kernel), "kernel": one_kernel}

@@ -125,7 +125,11 @@ typedef struct rlk_logp_desc {
  * `desc` (0 if `desc` is NULL or invalid).  Layout, from the workspace base
  * (which must be 256-byte aligned):
  *   [0, 256)                     uint32 status words: [0] target-range flag,
- *                                [1] non-finite-LSE flag (nonzero = seen)
+ *                                [1] non-finite-LSE flag (nonzero = seen),
+ *                                [2] after rlk_logp_fwd_bwd's unit schedule:
+ *                                the blocks that computed their row's
+ *                                partials themselves (0 when every exchange
+ *                                completed)
  *   [256, 256 + P)               float pmax[N][T]  per-tile maxima
  *   [256 + P, 256 + 2P)          float psum[N][T]  per-tile sums of exp(x - pmax)
  * where P = N*T*4 rounded up to a multiple of 256.  After rlk_logp_fwd the

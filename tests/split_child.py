@@ -50,6 +50,13 @@ def run_all(inp, wl, lm):
                                          out_dtype=dt, **kw),)
         out[f"one_{dt}"] = rlk.forward_backward(inp.logits, inp.targets, inp.mask, inp.grad,
                                                 out_dtype=dt, **kw)
+    # the unit schedule's fallback counter (status word 2) after a bf16 call
+    d = rlk.make_desc(wl.num_tokens, wl.real_vocab, wl.padded_vocab, wl.ld_logits, wl.num_tiles)
+    ws = torch.empty(rlk.rlk_logp_fwd_bwd_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    rlk.forward_backward(inp.logits, inp.targets, inp.mask, inp.grad, out_dtype=torch.bfloat16,
+                         workspace=ws, **kw)
+    torch.cuda.synchronize()
+    out["one_fallbacks"] = (ws[:12].view(torch.int32)[2:3].clone(),)
     gl = torch.linspace(-1.0, 1.0, wl.num_tokens, device=DEV)
     out["bwd_ex"] = (rlk.backward_ex(inp.logits, inp.targets, inp.mask, lse, ent, inp.grad, gl,
                                      -gl, **kw),)

@@ -1242,7 +1242,10 @@ __device__ __forceinline__ uint64_t pack_partial(float m, float s) {
   return ((uint64_t)__float_as_uint(s) << 32) | __float_as_uint(m);
 }
 
-__global__ __launch_bounds__(256) void fill_slots(uint64_t* __restrict__ slots, int64_t n) {
+// Sets every slot to kSlotEmpty and clears the fallback counter (status[2]).
+__global__ __launch_bounds__(256) void fill_slots(uint64_t* __restrict__ slots, int64_t n,
+                                                  uint32_t* __restrict__ status) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) status[2] = 0u;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     slots[i] = kSlotEmpty;
 }
@@ -1316,7 +1319,9 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
   }
   __syncthreads();
   if (s_fallback) {
-    // the row's T partials from the logits, by this block alone
+    // the row's T partials from the logits, by this block alone (counted in
+    // status[2], which fill_slots cleared)
+    if (threadIdx.x == 0) atomicAdd(status + 2, 1u);
     for (int32_t t0 = 0; t0 < num_tiles; t0 += kGroups) {
       const int32_t t = t0 + grp;
       int32_t flo = 0, fhi = 0;
@@ -1519,7 +1524,7 @@ hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
   const int64_t n_slots = (int64_t)a.num_rows * a.num_tiles;
   const int64_t fill_blocks = (n_slots + 255) / 256 < 8192 ? (n_slots + 255) / 256 : 8192;
   hipLaunchKernelGGL(fill_slots, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.slots,
-                     n_slots);
+                     n_slots, a.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // whole rows per launch: a row's units wait only for each other
