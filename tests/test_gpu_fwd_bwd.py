@@ -221,8 +221,19 @@ def test_unit_schedule_matches_row_schedule(case):
         inp.mask[1] = True
         inp.targets[4] = wl.real_vocab + 3  # a bad target on an active row
         inp.mask[4] = True
+    if n > 6:
+        # a bf16 NaN with every payload bit set: the largest-payload tile max there
+        # is (0xFFFF0000 widened), which must still differ from the empty-slot
+        # sentinel
+        inp.logits[5].view(torch.int16)[wl.real_vocab // 2] = -1
+    ws = torch.empty(rlk.rlk_logp_fwd_bwd_workspace_bytes(d), dtype=torch.uint8, device=DEV)
     for dt in (torch.float32, torch.bfloat16):
-        units = fused(inp, dt)
+        units = rlk.forward_backward(inp.logits, inp.targets, inp.mask, inp.grad,
+                                     real_vocab=wl.real_vocab, padded_vocab=wl.padded_vocab,
+                                     num_vocab_tiles=wl.num_tiles, out_dtype=dt, workspace=ws)
+        torch.cuda.synchronize()
+        # status word 2: no block had to compute its row's partials itself
+        assert ws[:12].view(torch.int32)[2].item() == 0, f"{case} {dt}: exchange fell back"
         assert_same_bits_nan(units, rows_schedule(inp, dt), f"{case} {dt} units vs rows")
         assert_same_bits_nan(units, separate(inp, dt), f"{case} {dt} units vs separate")
 
