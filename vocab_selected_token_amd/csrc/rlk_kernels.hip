@@ -1123,25 +1123,51 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
 constexpr uint64_t kSlotEmpty = ~0ull;
 constexpr int kUnitMaxPass = 4;  // tiles of up to 4 passes (80 chunks each) per lane group
 constexpr int kUnitWaves = 2;    // waves per block: 8 tiles per unit
+// Passes a lane keeps in registers; the rest wait in LDS.  With bf16 dX two
+// passes in LDS free 40 VGPRs (117 against 156), for 4 waves per SIMD instead of
+// 3 (32K rows: 3.28 against 3.45 ms).  With fp32 dX, whose stores are twice as
+// many, the registers win (5.43 against 5.99 ms).
+template <typename OutT>
+constexpr int kUnitRegPass = sizeof(OutT) == 2 ? 2 : kUnitMaxPass;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from global memory straight into LDS (nontemporal): lane i
+// of the wave writes bytes [16i, 16i + 16) after dst, which is the same for
+// the whole wave.  Completion is counted by vmcnt, like any load.
+__device__ __forceinline__ void load_chunk_to_lds(const uint4* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 2);
+}
 
 // The chunks one lane holds for its tile: slot (p, k) is chunk
 // base0 + p * kPassChunks + k * 16 + gl, plus the chunk cut by a tile bound
-// (lane 0: the head chunk, lane 1: the tail chunk) in qe.
-template <int kMaxPass>
+// (lane 0: the head chunk, lane 1: the tail chunk) in qe.  Passes below kRegPass
+// are kept in registers, the others in the wave's LDS area: slot (p, k) at
+// lds + ((p - kRegPass) * kChunks + k) * 1024 + 16 * lane.
+template <int kMaxPass, int kRegPass>
 struct TileRegs {
-  uint4 q[kMaxPass][kChunks];
+  uint4 q[kRegPass][kChunks];
   uint4 qe;
+  char* lds;       // this wave's LDS area (unused when kRegPass == kMaxPass)
   int32_t c_tail;  // this lane's tail chunk (its dX is written here), or -1
   int32_t base0, cf_lo, cf_hi, npass;
+  __device__ __forceinline__ uint4 chunk(int p, int k) const {
+    if (p < kRegPass) return q[p < kRegPass ? p : 0][k];
+    return *reinterpret_cast<const uint4*>(lds + ((p - kRegPass) * kChunks + k) * 1024 +
+                                           (threadIdx.x & 63) * 16);
+  }
 };
 
 // tile_partial's loads and arithmetic with every pass loaded up front and kept
 // (npass <= kMaxPass); the same fold order -- the cut chunk, then the passes in
-// ascending order -- and the same group reduction, so the same bits.
-template <int kMaxPass>
+// ascending order -- and the same group reduction, so the same bits.  The
+// register passes' loads go out first, so that folding them waits only for
+// them; the LDS passes are read back after all loads have landed.
+template <int kMaxPass, int kRegPass>
 __device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp, int32_t lo,
-                                                  int32_t hi, int gl, TileRegs<kMaxPass>& r,
-                                                  float& gm_out, float& ls_out) {
+                                                  int32_t hi, int gl,
+                                                  TileRegs<kMaxPass, kRegPass>& r, float& gm_out,
+                                                  float& ls_out) {
   float m = kNegInf, s = 0.0f, a = 0.0f;
   r.cf_lo = (lo + 7) >> 3;
   r.cf_hi = hi >> 3;
@@ -1162,13 +1188,34 @@ __device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp
   }
   if (c >= 0) r.qe = load_stream(rowp + c);
 #pragma unroll
-  for (int p = 0; p < kMaxPass; ++p)
+  for (int p = 0; p < kRegPass; ++p)
     if (p < r.npass) load_pass<true>(r.q[p], rowp, r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl);
+#pragma unroll
+  for (int p = kRegPass; p < kMaxPass; ++p)
+    if (p < r.npass) {
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k) {  // load_pass's clamped addresses
+        const int32_t cc = r.base0 + p * kPassChunks + k * kGroupLanes + gl;
+        load_chunk_to_lds(rowp + min(max(cc, r.cf_lo), r.cf_hi - 1),
+                          r.lds + ((p - kRegPass) * kChunks + k) * 1024);
+      }
+    }
   if (c >= 0) fold_edge<false>(r.qe, e_lo, e_hi, m, s, a);
 #pragma unroll
-  for (int p = 0; p < kMaxPass; ++p)
+  for (int p = 0; p < kRegPass; ++p)
     if (p < r.npass)
       fold_pass<false>(r.q[p], r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
+  if (kRegPass < kMaxPass) {
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS passes have landed
+#pragma unroll
+    for (int p = kRegPass; p < kMaxPass; ++p)
+      if (p < r.npass) {
+        uint4 q[kChunks];
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) q[k] = r.chunk(p, k);
+        fold_pass<false>(q, r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
+      }
+  }
   float la;
   group_reduce<false>(m, s, a, gm_out, ls_out, la);
 }
@@ -1198,8 +1245,8 @@ __device__ __forceinline__ void store_chunk(OutT* out, const float (&d)[8], int 
 // NaN on a row with a bad target, else -g exp(x - L) per column with the
 // target's column g (1 - exp(x_t - L)) -- dlogits_chunk's arithmetic.  The
 // tail chunk, which may reach past V_real, takes dlogits_chunk itself.
-template <int kMaxPass, typename OutT>
-__device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass>& r, int gl,
+template <int kMaxPass, int kRegPass, typename OutT>
+__device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>& r, int gl,
                                              OutT* __restrict__ orow, bool act, bool bad, float L,
                                              float g, int32_t tgt, int32_t real_vocab,
                                              int32_t padded_vocab) {
@@ -1215,7 +1262,7 @@ __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass>& r, int gl
       float d[8];
       if (act && !bad) {
         float x[8];
-        unpack8(r.q[p][k], x);
+        unpack8(r.chunk(p, k), x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[e] = ng * exp2_hw((x[e] - L) * kLog2e);
         if (tgt >= j0 && tgt < j0 + 8) {
@@ -1250,7 +1297,7 @@ __global__ __launch_bounds__(256) void fill_slots(uint64_t* __restrict__ slots, 
     slots[i] = kSlotEmpty;
 }
 
-template <typename OutT, int kMaxPass, int kUnitWaves>
+template <typename OutT, int kMaxPass, int kRegPass, int kUnitWaves>
 __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t real_vocab,
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t units_per_row,
@@ -1265,6 +1312,9 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
   __shared__ __align__(16) float s_sv[64];
   __shared__ float s_lse;
   __shared__ int s_fallback;
+  constexpr int kLdsPass = kMaxPass - kRegPass;
+  __shared__ __attribute__((aligned(16))) char s_pass[kUnitWaves * (kLdsPass > 0 ? kLdsPass : 1) *
+                                                      kChunks * 1024];
   const int64_t u = unit_begin + blockIdx.x;
   const int32_t row = (int32_t)(u / units_per_row);
   const int32_t unit = (int32_t)(u - (int64_t)row * units_per_row);
@@ -1288,9 +1338,10 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
   // 1. this unit's tiles, kept in registers
   int32_t lo = 0, hi = 0;
   if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
-  TileRegs<kMaxPass> tr;
+  TileRegs<kMaxPass, kRegPass> tr;
+  tr.lds = s_pass + wave * kLdsPass * kChunks * 1024;
   float gm, ls;
-  tile_partial_regs<kMaxPass>(rowp, lo, hi, gl, tr, gm, ls);
+  tile_partial_regs<kMaxPass, kRegPass>(rowp, lo, hi, gl, tr, gm, ls);
   uint64_t* __restrict__ rs = slots + (int64_t)row * num_tiles;
   // 2. publish
   if (tile < num_tiles && gl == 0)
@@ -1360,7 +1411,8 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
   if (tile >= num_tiles) return;
   const float L = act ? Lrow : 0.0f;
   OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
-  tile_dx_regs<kMaxPass, OutT>(tr, gl, orow, act, bad, L, g, tgt, real_vocab, padded_vocab);
+  tile_dx_regs<kMaxPass, kRegPass, OutT>(tr, gl, orow, act, bad, L, g, tgt, real_vocab,
+                                         padded_vocab);
   // chunks that start at or past V_real inside this tile's padded bounds: +0
   int32_t plo, phi;
   if (tile_width) {
@@ -1534,7 +1586,8 @@ hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
   for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
     const int64_t nr = a.num_rows - r0 < rows_per_launch ? a.num_rows - r0 : rows_per_launch;
-    hipLaunchKernelGGL((fwd_bwd_units<OutT, kUnitMaxPass, kUnitWaves>), dim3((unsigned)(nr * upr)),
+    hipLaunchKernelGGL((fwd_bwd_units<OutT, kUnitMaxPass, kUnitRegPass<OutT>, kUnitWaves>),
+                       dim3((unsigned)(nr * upr)),
                        dim3(kUnitWaves * 64), 0, stream, x, a.ld / 8, a.real_vocab,
                        a.padded_vocab, a.num_tiles, a.tile_width, upr, a.targets, a.mask,
                        a.ignore_index, a.grad, a.logp, a.lse, dl, a.ld_d, a.status, a.slots, spin,
