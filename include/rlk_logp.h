@@ -252,9 +252,9 @@ rlk_status rlk_logp_bwd_ex(const rlk_logp_desc* desc, const void* logits, const 
  * Two schedules, the same bits:
  *   - units (T <= 64 tiles of 8 to about 2,500 columns, e.g. 64 tiles over a
  *     152,576-column row): a block takes 8 consecutive tiles of a row, keeps
- *     their logits in registers, exchanges its tiles' (max, sumexp) partials
+ *     their logits on chip, exchanges its tiles' (max, sumexp) partials
  *     with the row's other blocks through 64-bit slots in the workspace, and
- *     writes dX from the registers.  A block waits for its row's slots a
+ *     writes dX from what it kept.  A block waits for its row's slots a
  *     bounded number of polls (environment variable RLK_FB_SPIN_LIMIT, read
  *     once per process, default 16384; 0 skips the wait) and past it computes
  *     the row's partials itself.

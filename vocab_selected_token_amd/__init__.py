@@ -452,7 +452,7 @@ def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,
     Bitwise the outputs of forward() then backward().  With the default workspace
     (rlk_logp_fwd_bwd_workspace_bytes) the unit schedule runs where the geometry
     takes it (T <= 64 tiles of 8 to about 2,500 columns): blocks of 8 tiles keep
-    their logits in registers and exchange partials through the workspace; a
+    their logits on chip and exchange partials through the workspace; a
     256-byte workspace selects one block per row."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")

@@ -1085,9 +1085,9 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
 
 // ---------------------------------------------------------------------------
 // Forward and backward in one launch, split across blocks: one block owns a
-// unit of kUnitWaves * 4 consecutive tiles of one row and keeps them in
-// registers from the read to the dX write, so HBM sees exactly one read of the
-// logits and one write of dX.
+// unit of kUnitWaves * 4 consecutive tiles of one row and keeps them on chip
+// (registers, and LDS for part of them) from the read to the dX write, so HBM
+// sees exactly one read of the logits and one write of dX.
 //   1. each 16-lane group reduces its tile with the stage-1 code (lane
 //      mapping, fold order and rotate tree of tile_partial), holding every
 //      chunk it loads;
@@ -1097,7 +1097,7 @@ __global__ __launch_bounds__(kFbThreads) void fwd_bwd_rows(
 //   3. wave 0 polls the row's T <= 64 slots (one per lane, relaxed atomic
 //      loads at agent scope) until none is empty, then merges them with the
 //      stage-2 arithmetic;
-//   4. the block writes dX of its columns from the registers.
+//   4. the block writes dX of its columns from what it kept.
 // A pair is a single 64-bit access, so a reader sees either the sentinel or
 // both halves of the partial: no fence is needed between the data and a flag
 // (a device-scope release would write back the L2 full of dX lines), only the
@@ -1239,7 +1239,7 @@ __device__ __forceinline__ void store_chunk(OutT* out, const float (&d)[8], int 
   }
 }
 
-// dX of the tile's chunks from the registers.  A full chunk lies inside the
+// dX of the tile's chunks from what the lane kept.  A full chunk lies inside the
 // real columns, so dlogits_chunk reduces to one of three forms, chosen once per
 // row (act and bad are the same for the whole block): +0 on an inactive row,
 // NaN on a row with a bad target, else -g exp(x - L) per column with the
@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
     x_t = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rowp)[tgt] << 16);
   const float g = act ? grad[row] : 0.0f;
 
-  // 1. this unit's tiles, kept in registers
+  // 1. this unit's tiles, kept on chip
   int32_t lo = 0, hi = 0;
   if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
   TileRegs<kMaxPass, kRegPass> tr;
