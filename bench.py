@@ -202,9 +202,12 @@ def cpu_baseline(inp, wl, max_seconds: float, extended=None, one_pass=False,
         fb, bb = b["fwd"], b["bwd"]
         if one_pass:  # one read of each logit for the whole step: charge it to the forward
             bb = algorithmic_bytes_one_pass(sub) - fb
-        if extended is not None:  # as the GPU line counts it: every row read again
-            fb += 4 * len(rows)
-            bb += (len(rows) - int(act.sum())) * wl.real_vocab * 2 + 12 * len(rows)
+        if extended is not None:  # as the GPU line counts it
+            fb += 4 * len(rows)  # entropy out
+            if one_pass:  # grad_lse and grad_ent read; no logit read again
+                bb += 8 * len(rows)
+            else:  # every row read again, and the entropy read back
+                bb += (len(rows) - int(act.sum())) * wl.real_vocab * 2 + 12 * len(rows)
         return t1 - t0, t2 - t1, fb, bb
 
     def sweep(nthreads, seconds):
@@ -419,7 +422,8 @@ def main() -> int:
                          "rlk_logp_fwd + rlk_logp_bwd")
     ap.add_argument("--extended", action="store_true",
                     help="time rlk_logp_fwd_ex + rlk_logp_bwd_ex (entropy output; logp, LSE "
-                         "and entropy gradients) instead of rlk_logp_fwd + rlk_logp_bwd")
+                         "and entropy gradients) instead of rlk_logp_fwd + rlk_logp_bwd; with "
+                         "--one-pass, rlk_logp_fwd_bwd_ex")
     ap.add_argument("--library-gemm", action="store_true",
                     help="LM-head workload: also time the library GEMM of the same shape")
     ap.add_argument("--no-sha", action="store_true",
@@ -486,11 +490,10 @@ def main() -> int:
     if (one_pass or extended) and not wl.backward:
         log("bench: --one-pass and --extended need a forward+backward workload")
         return 2
-    if one_pass and extended:
-        log("bench: --one-pass and --extended are separate schedules")
-        return 2
     if extended:
-        ws = torch.empty(rlk.rlk_logp_ex_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(rlk.rlk_logp_ex_workspace_bytes(desc),
+                             rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(desc) if one_pass else 0),
+                         dtype=torch.uint8, device=dev)
         ent = torch.empty(n, dtype=torch.float32, device=dev)
         gx = torch.Generator(device=dev).manual_seed(wl.seed + 7)
         g_lse = torch.randn(n, generator=gx, device=dev)
@@ -500,6 +503,13 @@ def main() -> int:
         b, m = inps[i % 2], masks[i % 2]
         if events:
             events[0].record(stream)
+        if one_pass and extended:
+            rlk.rlk_logp_fwd_bwd_ex(desc, b.logits, b.targets, m, b.grad, g_lse, g_ent, logp, lse,
+                                    ent, dl, ld_d, code, ws, stream)
+            if events:
+                events[1].record(stream)
+                events[2].record(stream)
+            return
         if one_pass:
             rlk.rlk_logp_fwd_bwd(desc, b.logits, b.targets, m, b.grad, logp, lse, dl, ld_d, code,
                                  ws, stream)
@@ -590,15 +600,17 @@ def main() -> int:
         shas = fingerprints(rlk, wl, inps[0], masks[0])
 
     if one_pass:
-        total_bytes = algorithmic_bytes_one_pass(wl)
+        # with the extended form: the entropy written, grad_lse and grad_ent read
+        total_bytes = algorithmic_bytes_one_pass(wl) + (12 * n if extended else 0)
         value = total_bytes / (ms_step * 1e-3) / 1e9
         k_gbs = total_bytes / (fwd_ms * 1e-3) / 1e9
-        kernels = {one_kernel: {"ms": round(fwd_ms, 4), "GB/s": round(k_gbs, 1),
-                                "bytes": total_bytes,
-                                "fallback_blocks": unit_fallbacks(ws, one_kernel)}}
+        kname = one_kernel + ("_ex" if extended else "")
+        kernels = {kname: {"ms": round(fwd_ms, 4), "GB/s": round(k_gbs, 1),
+                           "bytes": total_bytes,
+                           "fallback_blocks": unit_fallbacks(ws, one_kernel)}}
         roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic(one_kernel), "kernel": one_kernel}
+                    "traffic": None if extended else read_traffic(one_kernel), "kernel": kname}
     else:
         if extended:  # every row's logits are read again (the LSE and entropy terms reach all)
             nb = dict(nb)
@@ -652,9 +664,12 @@ def main() -> int:
                    "real_vocab": wl.real_vocab, "padded_vocab": wl.padded_vocab,
                    "vocab_tiles": wl.num_tiles, "virtual_shards": args.shards,
                    "dlogits_dtype": wl.dlogits_dtype, "parallelism": "single-gpu",
-                   "schedule": "one launch (rlk_logp_fwd_bwd)" if one_pass
-                   else ("rlk_logp_fwd_ex then rlk_logp_bwd_ex (entropy; logp, LSE and entropy "
-                         "gradients)" if extended else "rlk_logp_fwd then rlk_logp_bwd")},
+                   "schedule": ("one launch (rlk_logp_fwd_bwd_ex: entropy; logp, LSE and "
+                                "entropy gradients)" if one_pass and extended
+                                else "one launch (rlk_logp_fwd_bwd)" if one_pass
+                                else "rlk_logp_fwd_ex then rlk_logp_bwd_ex (entropy; logp, LSE "
+                                "and entropy gradients)" if extended
+                                else "rlk_logp_fwd then rlk_logp_bwd")},
         "tokens_per_s": round(n / (ms_step * 1e-3), 1),
         "step_ms_stream": step_spread,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),

@@ -281,6 +281,34 @@ rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
                             int64_t ld_dlogits, rlk_dtype dlogits_dtype, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* The extended forward and backward in one launch: bitwise the outputs of
+ * rlk_logp_fwd_ex followed by rlk_logp_bwd_ex on the same arguments (logp,
+ * LSE, entropy H, and the gradient of a loss reading all three), for a caller
+ * that has the three upstream gradients before the forward.  Where the geometry
+ * takes the unit schedule (as for rlk_logp_fwd_bwd) and the workspace holds its
+ * slots, one launch reads the logits once; otherwise the two extended calls
+ * run, with the same bits.  This single-pass schedule is not on the pages; the
+ * contract is [PR289]'s, with the extensions of rlk_logp_fwd_ex/_bwd_ex.
+ *   desc, logits, targets, active_mask   as for rlk_logp_fwd_ex.
+ *   grad_logp, grad_lse, grad_ent        (device) float [N] each, or NULL
+ *               (zero); at least one non-NULL; as for rlk_logp_bwd_ex.
+ *   logp, lse, entropy                   (device) float [N] out.
+ *   dlogits, ld_dlogits, dlogits_dtype   out, as for rlk_logp_bwd_ex.
+ *   workspace   >= rlk_logp_fwd_bwd_ex_workspace_bytes(desc) bytes, 256-byte
+ *               aligned: 256 + 16 N T with the unit schedule (two slot
+ *               arrays), else rlk_logp_ex_workspace_bytes(desc); with less
+ *               than the first but at least the second the two calls run.
+ * Errors as for rlk_logp_fwd_ex and rlk_logp_bwd_ex, all returned before any
+ * launch; with RLK_FLAG_VALIDATE the status words are checked once, after
+ * both steps (target range and non-finite LSE). */
+size_t rlk_logp_fwd_bwd_ex_workspace_bytes(const rlk_logp_desc* desc);
+rlk_status rlk_logp_fwd_bwd_ex(const rlk_logp_desc* desc, const void* logits,
+                               const int32_t* targets, const uint8_t* active_mask,
+                               const float* grad_logp, const float* grad_lse,
+                               const float* grad_ent, float* logp, float* lse, float* entropy,
+                               void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Fused LM-head variant: the logits are z = hidden . weight^T, taken in fp32
  * from bf16 MFMA products and never written to memory.  The pages name an
  * optional fused kernel without describing it ([I323] "Validation Boundary");

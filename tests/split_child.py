@@ -60,6 +60,12 @@ def run_all(inp, wl, lm):
     gl = torch.linspace(-1.0, 1.0, wl.num_tokens, device=DEV)
     out["bwd_ex"] = (rlk.backward_ex(inp.logits, inp.targets, inp.mask, lse, ent, inp.grad, gl,
                                      -gl, **kw),)
+    # the extended one launch, and its fallback counter
+    wse = torch.empty(rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    out["one_ex"] = rlk.forward_backward_ex(inp.logits, inp.targets, inp.mask, inp.grad, gl, -gl,
+                                            out_dtype=torch.bfloat16, workspace=wse, **kw)
+    torch.cuda.synchronize()
+    out["one_ex_fallbacks"] = (wse[:12].view(torch.int32)[2:3].clone(),)
     h, w, tg, v_real, v_pad, t = lm
     out["lmhead"] = rlk.fused_lmhead(h, w, tg, real_vocab=v_real, padded_vocab=v_pad,
                                      num_vocab_tiles=t)

@@ -291,6 +291,49 @@ def test_fwd_bwd_host_validation():
                          None, stream=s)
 
 
+def test_fwd_bwd_ex_host_validation():
+    a = _FakeTensor(0x10000000)
+    s = _NoStream()
+    ok = desc(num_tokens=8, num_vocab_tiles=64)
+    part = (8 * 64 * 4 + 255) // 256 * 256
+    # the unit schedule's two slot arrays where the geometry fits, else the two
+    # extended calls' workspace
+    assert rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(ok) == 256 + 2 * 8 * 64 * 8
+    wide = desc(num_tokens=8, real_vocab=4000, padded_vocab=4096, ld_logits=4096,
+                num_vocab_tiles=1)
+    assert rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(wide) == 256 + 3 * ((8 * 4 + 255) // 256 * 256)
+    assert rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(desc(num_vocab_tiles=1024)) == \
+        rlk.rlk_logp_ex_workspace_bytes(desc(num_vocab_tiles=1024))
+    assert rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(desc(num_vocab_tiles=0)) == 0
+    ws = _FakeTensor(0x20000000, 256 + 2 * 8 * 64 * 8)
+    f32 = rlk.RLK_DTYPE_F32
+
+    def call(d=ok, logits=a, tgt=a, g=a, gl=None, gh=None, logp=a, lse=a, ent=a, dl=a,
+             ld_d=1024, dt=f32, w=ws):
+        with pytest.raises(rlk.RlkError) as ei:
+            rlk.rlk_logp_fwd_bwd_ex(d, logits, tgt, None, g, gl, gh, logp, lse, ent, dl, ld_d, dt,
+                                    w, stream=s)
+        return ei.value.status
+
+    for kw, code in BAD_DESCS:
+        assert call(d=desc(**kw)) == code, kw
+    assert call(dt=7) == rlk.RLK_ERR_DTYPE
+    assert call(ld_d=1016) == rlk.RLK_ERR_BAD_SHAPE
+    assert call(ld_d=1028) == rlk.RLK_ERR_ALIGNMENT
+    for name in ("logits", "tgt", "logp", "lse", "ent", "dl"):
+        assert call(**{name: None}) == rlk.RLK_ERR_NULL_POINTER, name
+    assert call(g=None) == rlk.RLK_ERR_NULL_POINTER  # no gradient at all
+    assert call(w=None) == rlk.RLK_ERR_WORKSPACE
+    # below the two calls' workspace (which is below the unit schedule's)
+    assert call(w=_FakeTensor(0x20000000, 256 + 3 * part - 1)) == rlk.RLK_ERR_WORKSPACE
+    assert call(w=_FakeTensor(0x20000040, 256 + 2 * 8 * 64 * 8)) == rlk.RLK_ERR_ALIGNMENT
+    assert call(logits=_FakeTensor(0x10000008)) == rlk.RLK_ERR_ALIGNMENT
+    assert call(gl=_FakeTensor(0x10000002)) == rlk.RLK_ERR_ALIGNMENT
+    # an empty batch is a no-op
+    rlk.rlk_logp_fwd_bwd_ex(desc(num_tokens=0), None, None, None, None, None, None, None, None,
+                            None, None, 1024, f32, None, stream=s)
+
+
 def test_extended_forward_and_backward_host_validation():
     a = _FakeTensor(0x10000000)
     s = _NoStream()

@@ -37,6 +37,7 @@ RLK_FLAG_VALIDATE = 1
 EXPORTED = ("rlk_logp_workspace_bytes", "rlk_logp_fwd", "rlk_logp_bwd",
             "rlk_logp_ex_workspace_bytes", "rlk_logp_fwd_ex", "rlk_logp_bwd_ex",
             "rlk_logp_fwd_bwd_workspace_bytes", "rlk_logp_fwd_bwd",
+            "rlk_logp_fwd_bwd_ex_workspace_bytes", "rlk_logp_fwd_bwd_ex",
             "rlk_logp_fused_lmhead_workspace_bytes", "rlk_logp_fused_lmhead",
             "rlk_logp_tile_geometry", "rlk_status_string", "rlk_last_error_detail",
             "rlk_logp_fwd_noalloc")
@@ -83,6 +84,11 @@ def _load() -> ctypes.CDLL:
     lib.rlk_logp_fwd_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i64, ctypes.c_int, vp, sz,
                                      vp]
     lib.rlk_logp_fwd_bwd.restype = ctypes.c_int
+    lib.rlk_logp_fwd_bwd_ex_workspace_bytes.argtypes = [dp]
+    lib.rlk_logp_fwd_bwd_ex_workspace_bytes.restype = sz
+    lib.rlk_logp_fwd_bwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                        ctypes.c_int, vp, sz, vp]
+    lib.rlk_logp_fwd_bwd_ex.restype = ctypes.c_int
     lib.rlk_logp_fused_lmhead_workspace_bytes.argtypes = [dp]
     lib.rlk_logp_fused_lmhead_workspace_bytes.restype = sz
     lib.rlk_logp_fused_lmhead.argtypes = [dp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
@@ -179,6 +185,21 @@ def rlk_logp_fwd_bwd(desc, logits, targets, active_mask, grad_logp, logp, lse, d
                                  _ptr(active_mask), _ptr(grad_logp), _ptr(logp), _ptr(lse),
                                  _ptr(dlogits), ld_dlogits, dlogits_dtype, _ptr(workspace),
                                  ws_bytes, _stream(stream)))
+
+
+def rlk_logp_fwd_bwd_ex_workspace_bytes(desc: rlk_logp_desc) -> int:
+    return int(_lib.rlk_logp_fwd_bwd_ex_workspace_bytes(ctypes.byref(desc)))
+
+
+def rlk_logp_fwd_bwd_ex(desc, logits, targets, active_mask, grad_logp, grad_lse, grad_ent, logp,
+                        lse, entropy, dlogits, ld_dlogits: int, dlogits_dtype: int, workspace,
+                        stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rlk_logp_fwd_bwd_ex(ctypes.byref(desc), _ptr(logits), _ptr(targets),
+                                    _ptr(active_mask), _ptr(grad_logp), _ptr(grad_lse),
+                                    _ptr(grad_ent), _ptr(logp), _ptr(lse), _ptr(entropy),
+                                    _ptr(dlogits), ld_dlogits, dlogits_dtype, _ptr(workspace),
+                                    ws_bytes, _stream(stream)))
 
 
 def rlk_logp_fused_lmhead_workspace_bytes(desc: rlk_logp_desc) -> int:
@@ -477,6 +498,40 @@ def forward_backward(logits: torch.Tensor, targets: torch.Tensor, active_mask,
     rlk_logp_fwd_bwd(desc, logits, targets, _u8_mask(active_mask), grad_logp, logp, lse, dl, ld_d,
                      code, workspace, stream)
     return logp, lse, dl[:, :v_pad]
+
+
+def forward_backward_ex(logits: torch.Tensor, targets: torch.Tensor, active_mask,
+                        grad_logp=None, grad_lse=None, grad_ent=None, *, real_vocab: int,
+                        padded_vocab: int | None = None, num_vocab_tiles: int = 64,
+                        num_virtual_shards: int = 1, out_dtype=torch.float32,
+                        ignore_index: int = -100, validate: bool = False,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """(logp, lse, entropy, dlogits [N, V_pad]): forward_ex() then backward_ex() in one
+    launch where the unit schedule takes the geometry (the same bits either way);
+    absent gradients are zero, at least one must be given."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dlogits dtype must be torch.float32 or torch.bfloat16")
+    _check_vocab(logits, real_vocab, padded_vocab)
+    _check_inputs(logits, targets, active_mask, grad_logp=grad_logp, grad_lse=grad_lse,
+                  grad_ent=grad_ent)
+    n = logits.shape[0]
+    v_pad = padded_vocab or logits.shape[1]
+    desc = make_desc(n, real_vocab, v_pad, logits.stride(0), num_vocab_tiles, num_virtual_shards,
+                     ignore_index, validate)
+    ld_d = (v_pad + 7) // 8 * 8
+    logp = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+    ent = torch.empty(n, dtype=torch.float32, device=logits.device)
+    dl = torch.empty((n, ld_d), dtype=out_dtype, device=logits.device)
+    if workspace is None:
+        nbytes = rlk_logp_fwd_bwd_ex_workspace_bytes(desc)
+        if nbytes == 0:
+            raise ValueError(f"invalid rlk_logp_desc: {rlk_last_error_detail()}")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
+    code = RLK_DTYPE_BF16 if out_dtype == torch.bfloat16 else RLK_DTYPE_F32
+    rlk_logp_fwd_bwd_ex(desc, logits, targets, _u8_mask(active_mask), grad_logp, grad_lse,
+                        grad_ent, logp, lse, ent, dl, ld_d, code, workspace, stream)
+    return logp, lse, ent, dl[:, :v_pad]
 
 
 def fused_lmhead(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,

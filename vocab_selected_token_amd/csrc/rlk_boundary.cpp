@@ -478,6 +478,122 @@ rlk_status rlk_logp_fwd_bwd(const rlk_logp_desc* desc, const void* logits,
 }
 
 // ---------------------------------------------------------------------------
+// The extended forward and backward in one launch.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Bytes of the two partial-slot arrays of the extended unit schedule (0 where
+// the geometry does not take it).
+size_t fwd_bwd_ex_slot_bytes(const rlk_logp_desc* d) { return 2 * fwd_bwd_slot_bytes(d); }
+
+}  // namespace
+
+size_t rlk_logp_fwd_bwd_ex_workspace_bytes(const rlk_logp_desc* desc) {
+  if (check_desc(desc) != RLK_OK) return 0;
+  const size_t units = kStatusBytes + fwd_bwd_ex_slot_bytes(desc);
+  const size_t calls = needed_workspace_ex(desc);
+  return fwd_bwd_ex_slot_bytes(desc) > 0 && units > calls ? units : calls;
+}
+
+rlk_status rlk_logp_fwd_bwd_ex(const rlk_logp_desc* desc, const void* logits,
+                               const int32_t* targets, const uint8_t* active_mask,
+                               const float* grad_logp, const float* grad_lse,
+                               const float* grad_ent, float* logp, float* lse, float* entropy,
+                               void* dlogits, int64_t ld_dlogits, rlk_dtype dlogits_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  rlk_status st = check_desc(desc);
+  if (st != RLK_OK) return st;
+  if (dlogits_dtype != RLK_DTYPE_F32 && dlogits_dtype != RLK_DTYPE_BF16)
+    return fail(RLK_ERR_DTYPE, "dlogits_dtype=%d is neither RLK_DTYPE_F32 nor RLK_DTYPE_BF16",
+                (int)dlogits_dtype);
+  if (ld_dlogits < desc->padded_vocab)
+    return fail(RLK_ERR_BAD_SHAPE, "ld_dlogits=%lld < padded_vocab=%lld", (long long)ld_dlogits,
+                (long long)desc->padded_vocab);
+  if (ld_dlogits % 8 != 0)
+    return fail(RLK_ERR_ALIGNMENT, "ld_dlogits=%lld is not a multiple of 8 elements",
+                (long long)ld_dlogits);
+  const int64_t n = desc->num_tokens;
+  if (n == 0) return ok();
+  if (!logits || !targets || !logp || !lse || !entropy || !dlogits)
+    return fail(RLK_ERR_NULL_POINTER, "logits, targets, logp, lse, entropy and dlogits must be "
+                                      "non-NULL");
+  if (!grad_logp && !grad_lse && !grad_ent)
+    return fail(RLK_ERR_NULL_POINTER, "at least one of grad_logp, grad_lse and grad_ent must be "
+                                      "non-NULL");
+  if (!workspace) return fail(RLK_ERR_WORKSPACE, "workspace is NULL");
+  const size_t slot_bytes = fwd_bwd_ex_slot_bytes(desc);
+  const bool units = slot_bytes > 0 && workspace_bytes >= kStatusBytes + slot_bytes;
+  if (!units && workspace_bytes < needed_workspace_ex(desc))
+    return fail(RLK_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes,
+                rlk_logp_fwd_bwd_ex_workspace_bytes(desc));
+  if (!aligned(logits, 16) || !aligned(dlogits, 16))
+    return fail(RLK_ERR_ALIGNMENT, "logits and dlogits must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(RLK_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) || !aligned(entropy, 4) ||
+      !aligned(grad_logp, 4) || !aligned(grad_lse, 4) || !aligned(grad_ent, 4))
+    return fail(RLK_ERR_ALIGNMENT, "targets, logp, lse, entropy and the gradients must be 4-byte "
+                                   "aligned");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint32_t* status = reinterpret_cast<uint32_t*>(workspace);
+  const bool validate = (desc->flags & RLK_FLAG_VALIDATE) != 0;
+  hipError_t e;
+  if (!units) {
+    // the geometry (or the workspace) does not take the unit schedule: the two
+    // extended calls, which give the same bits, with the status words cleared
+    // once before them and checked once after
+    if (n * rlk::bwd_col_blocks((int32_t)desc->padded_vocab) > kI32Max)
+      return fail(RLK_ERR_BAD_SHAPE, "num_tokens * column blocks too large for one launch");
+    rlk_logp_desc d1 = *desc;
+    d1.flags &= ~RLK_FLAG_VALIDATE;
+    if (validate) {
+      e = rlk::launch_clear_status(status, stream);
+      if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+    }
+    st = run_forward(&d1, logits, targets, active_mask, logp, lse, entropy, workspace,
+                     workspace_bytes, stream_ptr);
+    if (st != RLK_OK) return st;
+    st = run_backward(&d1, logits, targets, active_mask, lse, entropy, grad_logp, grad_lse,
+                      grad_ent, dlogits, ld_dlogits, dlogits_dtype, workspace, workspace_bytes,
+                      stream_ptr, true);
+    if (st != RLK_OK) return st;
+    if (validate) return finish_validate(status, stream, true);
+    return ok();
+  }
+
+  if (validate) {
+    e = rlk::launch_clear_status(status, stream);
+    if (e != hipSuccess) return hip_fail(e, "clear_status launch");
+  }
+  const int32_t T = desc->num_vocab_tiles;
+  rlk::FwdBwdArgs a;
+  a.logits = logits;
+  a.ld = desc->ld_logits;
+  a.num_rows = (int32_t)n;
+  a.real_vocab = (int32_t)desc->real_vocab;
+  a.padded_vocab = (int32_t)desc->padded_vocab;
+  a.num_tiles = T;
+  a.tile_width = (desc->padded_vocab % T == 0) ? (int32_t)(desc->padded_vocab / T) : 0;
+  a.targets = targets;
+  a.mask = active_mask;
+  a.ignore_index = desc->ignore_index;
+  a.grad = grad_logp;
+  a.logp = logp;
+  a.lse = lse;
+  a.dlogits = dlogits;
+  a.ld_d = ld_dlogits;
+  a.out_bf16 = dlogits_dtype == RLK_DTYPE_BF16;
+  a.status = status;
+  a.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kStatusBytes);
+  a.entropy = entropy;
+  a.grad_lse = grad_lse;
+  a.grad_ent = grad_ent;
+  e = rlk::launch_fwd_bwd(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "fwd_bwd_units launch");
+  if (validate) return finish_validate(status, stream, true);
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Fused LM-head variant.
 // ---------------------------------------------------------------------------
 namespace {

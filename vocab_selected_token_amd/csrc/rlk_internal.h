@@ -84,9 +84,17 @@ struct FwdBwdArgs {
   int64_t ld_d;
   bool out_bf16;
   uint32_t* status;
-  // Unit schedule: [num_rows][num_tiles] 64-bit partial slots, or null for the
-  // one-block-per-row schedule (the same bits either way).
+  // Unit schedule: [num_rows][num_tiles] 64-bit partial slots (two such arrays
+  // with the entropy), or null for the one-block-per-row schedule (the same
+  // bits either way).
   uint64_t* slots;
+  // The extended form (unit schedule only): entropy out [num_rows] (non-null:
+  // the forward of rlk_logp_fwd_ex); grad_lse / grad_ent (either non-null: the
+  // gradient of rlk_logp_bwd_ex, with grad, grad_lse and grad_ent each null =
+  // zero).
+  float* entropy = nullptr;
+  const float* grad_lse = nullptr;
+  const float* grad_ent = nullptr;
 };
 
 // Whether the unit schedule of the one-launch forward+backward takes this

@@ -1163,11 +1163,11 @@ struct TileRegs {
 // ascending order -- and the same group reduction, so the same bits.  The
 // register passes' loads go out first, so that folding them waits only for
 // them; the LDS passes are read back after all loads have landed.
-template <int kMaxPass, int kRegPass>
+template <int kMaxPass, int kRegPass, bool kEnt>
 __device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp, int32_t lo,
                                                   int32_t hi, int gl,
                                                   TileRegs<kMaxPass, kRegPass>& r, float& gm_out,
-                                                  float& ls_out) {
+                                                  float& ls_out, float& la_out) {
   float m = kNegInf, s = 0.0f, a = 0.0f;
   r.cf_lo = (lo + 7) >> 3;
   r.cf_hi = hi >> 3;
@@ -1200,11 +1200,11 @@ __device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp
                           r.lds + ((p - kRegPass) * kChunks + k) * 1024);
       }
     }
-  if (c >= 0) fold_edge<false>(r.qe, e_lo, e_hi, m, s, a);
+  if (c >= 0) fold_edge<kEnt>(r.qe, e_lo, e_hi, m, s, a);
 #pragma unroll
   for (int p = 0; p < kRegPass; ++p)
     if (p < r.npass)
-      fold_pass<false>(r.q[p], r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
+      fold_pass<kEnt>(r.q[p], r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
   if (kRegPass < kMaxPass) {
     __builtin_amdgcn_s_waitcnt(0);  // the LDS passes have landed
 #pragma unroll
@@ -1213,11 +1213,10 @@ __device__ __forceinline__ void tile_partial_regs(const uint4* __restrict__ rowp
         uint4 q[kChunks];
 #pragma unroll
         for (int k = 0; k < kChunks; ++k) q[k] = r.chunk(p, k);
-        fold_pass<false>(q, r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
+        fold_pass<kEnt>(q, r.base0 + p * kPassChunks, r.cf_lo, r.cf_hi, gl, m, s, a);
       }
   }
-  float la;
-  group_reduce<false>(m, s, a, gm_out, ls_out, la);
+  group_reduce<kEnt>(m, s, a, gm_out, ls_out, la_out);
 }
 
 // dX of 8 columns at out; n = columns to write (1..8).  bf16: one 16-byte
@@ -1245,12 +1244,18 @@ __device__ __forceinline__ void store_chunk(OutT* out, const float (&d)[8], int 
 // NaN on a row with a bad target, else -g exp(x - L) per column with the
 // target's column g (1 - exp(x_t - L)) -- dlogits_chunk's arithmetic.  The
 // tail chunk, which may reach past V_real, takes dlogits_chunk itself.
-template <int kMaxPass, int kRegPass, typename OutT>
+// With kExGrad the extended gradient instead (dlogits_chunk_ex's arithmetic,
+// the same forms per full chunk: +0 on a row no term reaches, NaN on a bad
+// target, else the LSE, entropy and logp terms); act then means "some term
+// reaches the row" and tgt is -1 on a row that is not effective-active.
+template <int kMaxPass, int kRegPass, typename OutT, bool kExGrad = false>
 __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>& r, int gl,
                                              OutT* __restrict__ orow, bool act, bool bad, float L,
                                              float g, int32_t tgt, int32_t real_vocab,
-                                             int32_t padded_vocab) {
+                                             int32_t padded_vocab, float gl_ = 0.0f,
+                                             float gh = 0.0f, float H = 0.0f) {
   const float ng = -g;
+  const float cc = gl_ - g;
 #pragma unroll
   for (int p = 0; p < kMaxPass; ++p) {
     if (p >= r.npass) break;
@@ -1260,7 +1265,30 @@ __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>&
       if (c < r.cf_lo || c >= r.cf_hi) continue;
       const int32_t j0 = c << 3;
       float d[8];
-      if (act && !bad) {
+      if (act && !bad && kExGrad) {
+        float x[8], pv[8], hv[8];
+        unpack8(r.chunk(p, k), x);
+        if (gh != 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = x[e] - L;
+            pv[e] = exp2_hw(t * kLog2e);
+            hv[e] = fmaf(pv[e], H, pv[e] * __builtin_fmaxf(t, -__FLT_MAX__));
+            d[e] = fmaf(-gh, hv[e], pv[e] * cc);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = exp2_hw((x[e] - L) * kLog2e);
+            hv[e] = 0.0f;
+            d[e] = pv[e] * cc;
+          }
+        }
+        if (tgt >= j0 && tgt < j0 + 8) {
+          const int e = tgt - j0;
+          d[e] = g * (1.0f - pv[e]) + fmaf(-gh, hv[e], pv[e] * gl_);
+        }
+      } else if (act && !bad) {
         float x[8];
         unpack8(r.chunk(p, k), x);
 #pragma unroll
@@ -1280,7 +1308,10 @@ __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>&
   if (r.c_tail >= 0) {
     const int32_t j0 = r.c_tail << 3;
     float d[8];
-    dlogits_chunk(r.qe, j0, act, bad, L, g, tgt, real_vocab, d);
+    if (kExGrad)
+      dlogits_chunk_ex(r.qe, j0, act, bad, L, g, gl_, gh, H, tgt, real_vocab, d);
+    else
+      dlogits_chunk(r.qe, j0, act, bad, L, g, tgt, real_vocab, d);
     store_chunk<OutT>(orow + j0, d, min(8, padded_vocab - j0));
   }
 }
@@ -1297,20 +1328,34 @@ __global__ __launch_bounds__(256) void fill_slots(uint64_t* __restrict__ slots, 
     slots[i] = kSlotEmpty;
 }
 
-template <typename OutT, int kMaxPass, int kRegPass, int kUnitWaves>
+// kEnt: the forward also gives each row's entropy (stage1_partials<true> and
+// stage2's merge_lanes_entropy); the third statistic of a tile travels in a
+// second slot array [N][T] right after the first, as the pair (a, max) -- the
+// max half keeps that slot, too, from ever holding the sentinel.
+// kExGrad: dX is rlk_logp_bwd_ex's extended gradient (grad_lse or grad_ent
+// given; any of grad, grad_lse and grad_ent may be null = zero), else the plain
+// gradient, as the separate extended backward chooses.
+template <typename OutT, int kMaxPass, int kRegPass, int kUnitWaves, bool kEnt, bool kExGrad>
 __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
     const uint4* __restrict__ logits, int64_t ld_chunks, int32_t real_vocab,
     int32_t padded_vocab, int32_t num_tiles, int32_t tile_width, int32_t units_per_row,
     const int32_t* __restrict__ targets, const uint8_t* __restrict__ mask, int32_t ignore_index,
-    const float* __restrict__ grad, float* __restrict__ logp, float* __restrict__ lse,
-    OutT* __restrict__ dlogits, int64_t ld_d, uint32_t* __restrict__ status,
-    uint64_t* __restrict__ slots, int32_t spin_limit, int64_t unit_begin) {
+    const float* __restrict__ grad, const float* __restrict__ grad_lse,
+    const float* __restrict__ grad_ent, float* __restrict__ logp, float* __restrict__ lse,
+    float* __restrict__ entropy, OutT* __restrict__ dlogits, int64_t ld_d,
+    uint32_t* __restrict__ status, uint64_t* __restrict__ slots, int64_t slots_b,
+    int32_t spin_limit, int64_t unit_begin) {
+  static_assert(kEnt || !kExGrad, "the extended gradient needs the entropy");
   constexpr int kGroups = kUnitWaves * kGroupsPerWave;  // tiles per unit
   __shared__ float s_m[64];
   __shared__ float s_s[64];
+  __shared__ float s_a[kEnt ? 64 : 1];
   __shared__ __align__(16) float s_e[64];
   __shared__ __align__(16) float s_sv[64];
+  __shared__ __align__(16) float s_d[kEnt ? 64 : 1];
+  __shared__ __align__(16) float s_av[kEnt ? 64 : 1];
   __shared__ float s_lse;
+  __shared__ float s_ent;
   __shared__ int s_fallback;
   constexpr int kLdsPass = kMaxPass - kRegPass;
   __shared__ __attribute__((aligned(16))) char s_pass[kUnitWaves * (kLdsPass > 0 ? kLdsPass : 1) *
@@ -1333,28 +1378,40 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
   float x_t = 0.0f;
   if (unit == 0 && threadIdx.x == 0 && act && !bad)
     x_t = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rowp)[tgt] << 16);
-  const float g = act ? grad[row] : 0.0f;
+  const float g = (act && (!kExGrad || grad)) ? grad[row] : 0.0f;
+  float g_l = 0.0f, g_h = 0.0f;
+  if (kExGrad) {
+    g_l = grad_lse ? grad_lse[row] : 0.0f;
+    g_h = grad_ent ? grad_ent[row] : 0.0f;
+  }
 
   // 1. this unit's tiles, kept on chip
   int32_t lo = 0, hi = 0;
   if (tile < num_tiles) tile_range(tile, tile_width, padded_vocab, num_tiles, real_vocab, lo, hi);
   TileRegs<kMaxPass, kRegPass> tr;
   tr.lds = s_pass + wave * kLdsPass * kChunks * 1024;
-  float gm, ls;
-  tile_partial_regs<kMaxPass, kRegPass>(rowp, lo, hi, gl, tr, gm, ls);
+  float gm, ls, la;
+  tile_partial_regs<kMaxPass, kRegPass, kEnt>(rowp, lo, hi, gl, tr, gm, ls, la);
   uint64_t* __restrict__ rs = slots + (int64_t)row * num_tiles;
+  uint64_t* __restrict__ rsb = slots + slots_b + (int64_t)row * num_tiles;
   // 2. publish
-  if (tile < num_tiles && gl == 0)
+  if (tile < num_tiles && gl == 0) {
     __hip_atomic_store(rs + tile, pack_partial(gm, ls), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (kEnt)
+      __hip_atomic_store(rsb + tile, pack_partial(gm, la), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // 3. the row's partials, merged in ascending tile order (wave 0)
   if (wave == 0) {
     bool ok = false;
-    uint64_t v = kSlotEmpty;
+    uint64_t v = kSlotEmpty, vb = kSlotEmpty;
     for (int32_t it = 0; it < spin_limit; ++it) {
-      if (lane < num_tiles)
+      if (lane < num_tiles) {
         v = __hip_atomic_load(rs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__all(lane >= num_tiles || v != kSlotEmpty)) {
+        if (kEnt) vb = __hip_atomic_load(rsb + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (__all(lane >= num_tiles || (v != kSlotEmpty && (!kEnt || vb != kSlotEmpty)))) {
         ok = true;
         break;
       }
@@ -1363,8 +1420,18 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
     if (ok) {
       const float mt = lane < num_tiles ? __uint_as_float((uint32_t)v) : kNegInf;
       const float st = lane < num_tiles ? __uint_as_float((uint32_t)(v >> 32)) : 0.0f;
-      const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
-      if (lane == 0) s_lse = L;
+      if (kEnt) {
+        const float at = lane < num_tiles ? __uint_as_float((uint32_t)(vb >> 32)) : 0.0f;
+        float H;
+        const float L = merge_lanes_entropy(mt, st, at, num_tiles, lane, s_e, s_sv, s_d, s_av, H);
+        if (lane == 0) {
+          s_lse = L;
+          s_ent = H;
+        }
+      } else {
+        const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
+        if (lane == 0) s_lse = L;
+      }
     }
     if (lane == 0) s_fallback = ok ? 0 : 1;
   }
@@ -1378,24 +1445,37 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
       int32_t flo = 0, fhi = 0;
       if (t < num_tiles) tile_range(t, tile_width, padded_vocab, num_tiles, real_vocab, flo, fhi);
       float fm, fs, fa;
-      tile_partial<true, 1>(rowp, flo, fhi, gl, fm, fs, fa);
+      tile_partial<true, 1, kEnt>(rowp, flo, fhi, gl, fm, fs, fa);
       if (t < num_tiles && gl == 0) {
         s_m[t] = fm;
         s_s[t] = fs;
+        if (kEnt) s_a[kEnt ? t : 0] = fa;
       }
     }
     __syncthreads();
     if (wave == 0) {
       const float mt = lane < num_tiles ? s_m[lane] : kNegInf;
       const float st = lane < num_tiles ? s_s[lane] : 0.0f;
-      const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
-      if (lane == 0) s_lse = L;
+      if (kEnt) {
+        const float at = lane < num_tiles ? s_a[kEnt ? lane : 0] : 0.0f;
+        float H;
+        const float L = merge_lanes_entropy(mt, st, at, num_tiles, lane, s_e, s_sv, s_d, s_av, H);
+        if (lane == 0) {
+          s_lse = L;
+          s_ent = H;
+        }
+      } else {
+        const float L = merge_lanes(mt, st, num_tiles, lane, s_e, s_sv);
+        if (lane == 0) s_lse = L;
+      }
     }
     __syncthreads();
   }
   const float Lrow = s_lse;
+  const float Hrow = kEnt ? s_ent : 0.0f;
   if (unit == 0 && threadIdx.x == 0) {
     lse[row] = Lrow;
+    if (kEnt) entropy[row] = Hrow;
     if (!act) {
       logp[row] = 0.0f;
     } else if (bad) {
@@ -1409,10 +1489,21 @@ __global__ __launch_bounds__(kUnitWaves * 64) void fwd_bwd_units(
 
   // 4. dX of this unit's columns
   if (tile >= num_tiles) return;
-  const float L = act ? Lrow : 0.0f;
   OutT* __restrict__ orow = dlogits + (int64_t)row * ld_d;
-  tile_dx_regs<kMaxPass, kRegPass, OutT>(tr, gl, orow, act, bad, L, g, tgt, real_vocab,
-                                         padded_vocab);
+  if (kExGrad) {
+    // the separate extended backward's row values: a row is reached by the logp
+    // term when effective-active, by the LSE and entropy terms when theirs are
+    // nonzero; the target term only on an effective-active row
+    const bool need = act || g_l != 0.0f || g_h != 0.0f;
+    const float L = need ? Lrow : 0.0f;
+    const float H = g_h != 0.0f ? Hrow : 0.0f;
+    tile_dx_regs<kMaxPass, kRegPass, OutT, true>(tr, gl, orow, need, bad, L, g, act ? tgt : -1,
+                                                 real_vocab, padded_vocab, g_l, g_h, H);
+  } else {
+    const float L = act ? Lrow : 0.0f;
+    tile_dx_regs<kMaxPass, kRegPass, OutT>(tr, gl, orow, act, bad, L, g, tgt, real_vocab,
+                                           padded_vocab);
+  }
   // chunks that start at or past V_real inside this tile's padded bounds: +0
   int32_t plo, phi;
   if (tile_width) {
@@ -1570,10 +1661,10 @@ bool fwd_bwd_units_fit(int32_t real_vocab, int32_t padded_vocab, int32_t num_til
 
 namespace {
 
-template <typename OutT>
+template <typename OutT, bool kEnt, bool kExGrad>
 hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
   constexpr int kGroups = kUnitWaves * kGroupsPerWave;
-  const int64_t n_slots = (int64_t)a.num_rows * a.num_tiles;
+  const int64_t n_slots = (int64_t)a.num_rows * a.num_tiles * (kEnt ? 2 : 1);
   const int64_t fill_blocks = (n_slots + 255) / 256 < 8192 ? (n_slots + 255) / 256 : 8192;
   hipLaunchKernelGGL(fill_slots, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.slots,
                      n_slots, a.status);
@@ -1584,18 +1675,26 @@ hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
   const int64_t rows_per_launch = launch_thread_limit() / (kUnitWaves * 64) / upr;
   const int32_t spin = fwd_bwd_spin_limit();
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
+  const int64_t slots_b = (int64_t)a.num_rows * a.num_tiles;
   for (int64_t r0 = 0; r0 < a.num_rows; r0 += rows_per_launch) {
     const int64_t nr = a.num_rows - r0 < rows_per_launch ? a.num_rows - r0 : rows_per_launch;
-    hipLaunchKernelGGL((fwd_bwd_units<OutT, kUnitMaxPass, kUnitRegPass<OutT>, kUnitWaves>),
-                       dim3((unsigned)(nr * upr)),
-                       dim3(kUnitWaves * 64), 0, stream, x, a.ld / 8, a.real_vocab,
-                       a.padded_vocab, a.num_tiles, a.tile_width, upr, a.targets, a.mask,
-                       a.ignore_index, a.grad, a.logp, a.lse, dl, a.ld_d, a.status, a.slots, spin,
-                       r0 * upr);
+    hipLaunchKernelGGL(
+        (fwd_bwd_units<OutT, kUnitMaxPass, kUnitRegPass<OutT>, kUnitWaves, kEnt, kExGrad>),
+        dim3((unsigned)(nr * upr)), dim3(kUnitWaves * 64), 0, stream, x, a.ld / 8, a.real_vocab,
+        a.padded_vocab, a.num_tiles, a.tile_width, upr, a.targets, a.mask, a.ignore_index, a.grad,
+        a.grad_lse, a.grad_ent, a.logp, a.lse, a.entropy, dl, a.ld_d, a.status, a.slots, slots_b,
+        spin, r0 * upr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <typename OutT>
+hipError_t launch_units_for(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
+  if (!a.entropy) return launch_units<OutT, false, false>(a, dl, stream);
+  if (a.grad_lse || a.grad_ent) return launch_units<OutT, true, true>(a, dl, stream);
+  return launch_units<OutT, true, false>(a, dl, stream);
 }
 
 }  // namespace
@@ -1603,8 +1702,8 @@ hipError_t launch_units(const FwdBwdArgs& a, OutT* dl, hipStream_t stream) {
 hipError_t launch_fwd_bwd(const FwdBwdArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   if (a.slots) {
-    if (a.out_bf16) return launch_units(a, reinterpret_cast<uint16_t*>(a.dlogits), stream);
-    return launch_units(a, reinterpret_cast<float*>(a.dlogits), stream);
+    if (a.out_bf16) return launch_units_for(a, reinterpret_cast<uint16_t*>(a.dlogits), stream);
+    return launch_units_for(a, reinterpret_cast<float*>(a.dlogits), stream);
   }
   const int64_t rows_per_launch = launch_thread_limit() / kFbThreads;
   const uint4* x = reinterpret_cast<const uint4*>(a.logits);
