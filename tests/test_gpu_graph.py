@@ -1,6 +1,7 @@
 """Every entry point called without RLK_FLAG_VALIDATE enqueues kernel launches
 only -- no allocation, no memset, no copy, no synchronisation -- so a caller can
-capture it into a HIP graph.  One graph holds a call of each entry point; it is
+capture it into a HIP graph.  One graph holds a call of each entry point (the
+one-launch calls in their unit schedule, whose slot fill is a kernel); it is
 replayed several times, with a different input set copied into the captured
 buffers before each replay and eager work in between, and every replay must give
 the bits of the same calls made eagerly on that input set.  Needs an MI355X."""
@@ -47,6 +48,8 @@ def test_graph_replays_match_eager():
     w_one = ws(rlk.rlk_logp_fwd_bwd_workspace_bytes(d3))
     w_ex = ws(rlk.rlk_logp_ex_workspace_bytes(d3))
     w_lm = ws(rlk.rlk_logp_fused_lmhead_workspace_bytes(d3))
+    w_onex = ws(rlk.rlk_logp_fwd_bwd_ex_workspace_bytes(d3))
+    assert rlk.rlk_logp_fwd_bwd_workspace_bytes(d3) > 256  # both one-launch calls: unit schedule
 
     def outputs():
         f = lambda: torch.empty(N, device=DEV)  # noqa: E731
@@ -55,7 +58,8 @@ def test_graph_replays_match_eager():
                 "d32": torch.empty((N, V_PAD), device=DEV), "logp1": f(), "lse1": f(),
                 "d1": torch.empty((N, V_PAD), dtype=torch.bfloat16, device=DEV),
                 "logpx": f(), "lsex": f(), "ent": f(), "dx": torch.empty((N, V_PAD), device=DEV),
-                "lpl": f(), "lsel": f()}
+                "lpl": f(), "lsel": f(), "logpy": f(), "lsey": f(), "enty": f(),
+                "dy": torch.empty((N, V_PAD), device=DEV)}
 
     def calls(o):
         x, tg, m, g = st["x"], st["tg"], st["m"], st["g"]
@@ -68,6 +72,8 @@ def test_graph_replays_match_eager():
         rlk.rlk_logp_bwd_ex(d3, x, tg, m, o["lsex"], o["ent"], g, gl, gh, o["dx"], V_PAD,
                             rlk.RLK_DTYPE_F32, w_ex)
         rlk.rlk_logp_fused_lmhead(d3, st["h"], st["w"], K, tg, m, o["lpl"], o["lsel"], w_lm)
+        rlk.rlk_logp_fwd_bwd_ex(d3, x, tg, m, g, gl, gh, o["logpy"], o["lsey"], o["enty"],
+                                o["dy"], V_PAD, rlk.RLK_DTYPE_F32, w_onex)
 
     def load(i):
         for k, v in sets[i].items():
@@ -83,6 +89,7 @@ def test_graph_replays_match_eager():
     # the one-launch schedule and the separate calls agree, as they must
     for r in refs:
         assert torch.equal(r["logp1"], r["logp"]) and torch.equal(r["d1"], r["d16"])
+        assert torch.equal(r["enty"], r["ent"]) and torch.equal(r["dy"], r["dx"])
 
     og = outputs()
     load(0)
