@@ -627,13 +627,18 @@ __device__ __forceinline__ void dlogits_chunk(const typename Cols<NC>::T& q, int
 // The extended gradient of the NC columns [j0, j0 + NC) of one row, with the
 // LSE and entropy terms (the derivatives of LSE and of H = -sum p log p):
 //   d_j = g ([j == t] - p_j) + gl p_j - gh p_j (log p_j + H),  log p_j = x_j - L
-// computed off the target as fma(-gh, fma(p_j, H, p_j u_j), p_j c), c = gl - g,
-// and at the target as g (1 - p_t) + fma(-gh, fma(p_t, H, p_t u_t), p_t gl),
-// with u_j = max(x_j - L, -FLT_MAX): a column at -inf has p = 0 and adds 0 to
-// every term (0 log 0 = 0).  Without an entropy term (gh == 0, uniform over the
-// row) it is p_j c and g (1 - p_t) + p_t gl.  `need` is false on a row that no
+// computed off the target as p_j fma(-gh, u_j, k) with k = gl - g - gh H fixed
+// for the row, and at the target as fma(p_t, fma(-gh, u_t, k), g), where
+// u_j = max(x_j - L, kLogpFloor): a column at -inf has p = 0 and adds 0 to every
+// term (0 log 0 = 0), and the floor keeps gh u finite.  Without an entropy term
+// (gh == 0, uniform over the row) it is p_j c, c = gl - g, and g (1 - p_t) + p_t gl
+// (H is not read there, so a row whose H is NaN keeps its other terms).  `need` is false on a row that no
 // term reaches (it stays +0 and is not read); `bad` marks an effective-active
 // row with a target outside [0, V_real) (NaN on its real columns).
+// Below every exponent whose exponential is nonzero in fp32 (about -103.3):
+// clamping log p there changes no column with p > 0.
+constexpr float kLogpFloor = -256.0f;
+
 template <int NC>
 __device__ __forceinline__ void dlogits_chunk_ex(const typename Cols<NC>::T& q, int32_t j0,
                                                  bool need, bool bad, float L, float g, float gl,
@@ -652,20 +657,21 @@ __device__ __forceinline__ void dlogits_chunk_ex(const typename Cols<NC>::T& q, 
     float x[NC];
     Cols<NC>::unpack(q, x);
     const float c = gl - g;
-    float p[NC], hv[NC];
+    float p[NC], q[NC];
     if (gh != 0.0f) {  // uniform over the row
+      const float k = c - gh * H;
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
         const float t = x[e] - L;
         p[e] = exp2_hw(t * kLog2e);
-        hv[e] = fmaf(p[e], H, p[e] * __builtin_fmaxf(t, -__FLT_MAX__));
-        d[e] = fmaf(-gh, hv[e], p[e] * c);
+        q[e] = fmaf(-gh, __builtin_fmaxf(t, kLogpFloor), k);
+        d[e] = p[e] * q[e];
       }
     } else {
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
         p[e] = exp2_hw((x[e] - L) * kLog2e);
-        hv[e] = 0.0f;
+        q[e] = 0.0f;
         d[e] = p[e] * c;
       }
     }
@@ -676,7 +682,7 @@ __device__ __forceinline__ void dlogits_chunk_ex(const typename Cols<NC>::T& q, 
     }
     if (tgt >= j0 && tgt < j0 + NC) {
       const int e = tgt - j0;
-      d[e] = g * (1.0f - p[e]) + fmaf(-gh, hv[e], p[e] * gl);
+      d[e] = gh != 0.0f ? fmaf(p[e], q[e], g) : g * (1.0f - p[e]) + p[e] * gl;
     }
   }
 }
@@ -1256,6 +1262,7 @@ __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>&
                                              float gh = 0.0f, float H = 0.0f) {
   const float ng = -g;
   const float cc = gl_ - g;
+  const float kk = cc - gh * H;  // read only where gh != 0
 #pragma unroll
   for (int p = 0; p < kMaxPass; ++p) {
     if (p >= r.npass) break;
@@ -1266,27 +1273,27 @@ __device__ __forceinline__ void tile_dx_regs(const TileRegs<kMaxPass, kRegPass>&
       const int32_t j0 = c << 3;
       float d[8];
       if (act && !bad && kExGrad) {
-        float x[8], pv[8], hv[8];
+        float x[8], pv[8], qv[8];
         unpack8(r.chunk(p, k), x);
         if (gh != 0.0f) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float t = x[e] - L;
             pv[e] = exp2_hw(t * kLog2e);
-            hv[e] = fmaf(pv[e], H, pv[e] * __builtin_fmaxf(t, -__FLT_MAX__));
-            d[e] = fmaf(-gh, hv[e], pv[e] * cc);
+            qv[e] = fmaf(-gh, __builtin_fmaxf(t, kLogpFloor), kk);
+            d[e] = pv[e] * qv[e];
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             pv[e] = exp2_hw((x[e] - L) * kLog2e);
-            hv[e] = 0.0f;
+            qv[e] = 0.0f;
             d[e] = pv[e] * cc;
           }
         }
         if (tgt >= j0 && tgt < j0 + 8) {
           const int e = tgt - j0;
-          d[e] = g * (1.0f - pv[e]) + fmaf(-gh, hv[e], pv[e] * gl_);
+          d[e] = gh != 0.0f ? fmaf(pv[e], qv[e], g) : g * (1.0f - pv[e]) + pv[e] * gl_;
         }
       } else if (act && !bad) {
         float x[8];
