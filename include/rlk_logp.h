@@ -43,8 +43,11 @@
  * Conventions shared by every call:
  *   - Ownership: the caller allocates and owns every buffer, device and host,
  *     including the workspace.  The library never allocates, frees or keeps a
- *     pointer after a call returns.  Its only global state is the per-thread
- *     error-detail string.
+ *     pointer after a call returns.  Its global state is the per-thread
+ *     error-detail string, two settings read once per process from the
+ *     environment (RLK_MAX_LAUNCH_THREADS below, RLK_FB_SPIN_LIMIT at
+ *     rlk_logp_fwd_bwd), and, for rlk_logp_fwd_noalloc only, a device array of
+ *     its own on each GPU it runs on.
  *   - Pointers marked (device) must be device-accessible memory of the device
  *     that is current on the calling thread; `desc` is a host pointer.
  *   - Streams: every call enqueues its kernels on `stream` (0 = the null
@@ -56,8 +59,11 @@
  *     outputs are always safe: a bad target yields NaN and no out-of-bounds
  *     read.  With RLK_FLAG_VALIDATE the call synchronises the stream and
  *     reports them as RLK_ERR_TARGET_RANGE / RLK_ERR_NONFINITE_LSE.
- *   - There is one code path and no fallback: if the GPU path cannot run, the
- *     call fails.
+ *   - There is one computation and no fallback to another: if the GPU path
+ *     cannot run, the call fails.  Where a call has more than one schedule
+ *     (rlk_logp_fwd_bwd, rlk_logp_fwd_bwd_ex), every schedule computes each
+ *     value with the same code in the same order and gives the same bits; the
+ *     geometry and the workspace passed decide which runs.
  *   - Graph capture: without RLK_FLAG_VALIDATE a call enqueues kernel launches
  *     only -- no allocation, memset, copy or synchronisation -- so it may be
  *     captured into a HIP graph and replayed; the replays read whatever the
@@ -126,10 +132,10 @@ typedef struct rlk_logp_desc {
  * (which must be 256-byte aligned):
  *   [0, 256)                     uint32 status words: [0] target-range flag,
  *                                [1] non-finite-LSE flag (nonzero = seen),
- *                                [2] after rlk_logp_fwd_bwd's unit schedule:
- *                                the blocks that computed their row's
- *                                partials themselves (0 when every exchange
- *                                completed)
+ *                                [2] after the unit schedule of
+ *                                rlk_logp_fwd_bwd or rlk_logp_fwd_bwd_ex: the
+ *                                blocks that computed their row's partials
+ *                                themselves (0 when every exchange completed)
  *   [256, 256 + P)               float pmax[N][T]  per-tile maxima
  *   [256 + P, 256 + 2P)          float psum[N][T]  per-tile sums of exp(x - pmax)
  * where P = N*T*4 rounded up to a multiple of 256.  After rlk_logp_fwd the
