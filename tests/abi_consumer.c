@@ -5,6 +5,8 @@
  *   - every virtual-shard count S gives the bits of S = 1;
  *   - logp = fp32(x[target]) - LSE exactly, +0.0 on inactive rows;
  *   - each backward row sums to about 0 (g (1 - sum softmax));
+ *   - rlk_logp_fwd_bwd gives the bits of rlk_logp_fwd then rlk_logp_bwd, and
+ *     rlk_logp_fwd_bwd_ex those of rlk_logp_fwd_ex then rlk_logp_bwd_ex;
  *   - host errors come back as status codes with a reason.
  * Prints one line per check and exits 0 only if all pass.  Built by the
  * package's build step; run by tests/test_gpu_abi_consumer.py.
@@ -149,6 +151,74 @@ int main(void) {
   printf("backward rows sum to ~0 (worst %.2e), zeros where inactive or padded: %s\n", worst,
          (worst < 1e-4 && zeros_ok) ? "ok" : "FAIL");
   failures += !(worst < 1e-4 && zeros_ok);
+
+  /* the one-launch calls: the same bits as the separate ones */
+  {
+    const size_t ws1_bytes = rlk_logp_fwd_bwd_workspace_bytes(&desc);
+    const size_t wse_bytes = rlk_logp_ex_workspace_bytes(&desc);
+    const size_t wsx_bytes = rlk_logp_fwd_bwd_ex_workspace_bytes(&desc);
+    float* gl = malloc(sizeof(float) * n);
+    float* gh = malloc(sizeof(float) * n);
+    for (int64_t r = 0; r < n; ++r) {
+      gl[r] = (float)((int)(next_u64() % 200) - 100) / 100.0f;
+      gh[r] = (float)((int)(next_u64() % 200) - 100) / 100.0f;
+    }
+    void *dws1, *dwse, *dwsx, *dgl, *dgh, *dent, *dent2, *dd2, *dd3;
+    CHECK_HIP(hipMalloc(&dws1, ws1_bytes));
+    CHECK_HIP(hipMalloc(&dwse, wse_bytes));
+    CHECK_HIP(hipMalloc(&dwsx, wsx_bytes));
+    CHECK_HIP(hipMalloc(&dgl, sizeof(float) * n));
+    CHECK_HIP(hipMalloc(&dgh, sizeof(float) * n));
+    CHECK_HIP(hipMalloc(&dent, sizeof(float) * n));
+    CHECK_HIP(hipMalloc(&dent2, sizeof(float) * n));
+    CHECK_HIP(hipMalloc(&dd2, sizeof(float) * n * ld));
+    CHECK_HIP(hipMalloc(&dd3, sizeof(float) * n * ld));
+    CHECK_HIP(hipMemcpy(dgl, gl, sizeof(float) * n, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dgh, gh, sizeof(float) * n, hipMemcpyHostToDevice));
+    float* d2 = malloc(sizeof(float) * n * ld);
+    float* d3 = malloc(sizeof(float) * n * ld);
+    float* ent = malloc(sizeof(float) * n);
+    float* ent2 = malloc(sizeof(float) * n);
+
+    CHECK_RLK(rlk_logp_fwd_bwd(&desc, dx, dtgt, dmask, dg, dlogp2, dlse2, dd2, ld, RLK_DTYPE_F32,
+                               dws1, ws1_bytes, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(logp2, dlogp2, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(lse2, dlse2, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(d2, dd2, sizeof(float) * n * ld, hipMemcpyDeviceToHost));
+    int same = memcmp(logp, logp2, sizeof(float) * n) == 0 &&
+               memcmp(lse, lse2, sizeof(float) * n) == 0;
+    for (int64_t r = 0; r < n; ++r)  /* columns [0, V_pad) of each row */
+      same &= memcmp(d + r * ld, d2 + r * ld, sizeof(float) * v_pad) == 0;
+    printf("rlk_logp_fwd_bwd bitwise equal to the two calls: %s\n", same ? "ok" : "FAIL");
+    failures += !same;
+
+    CHECK_RLK(rlk_logp_fwd_ex(&desc, dx, dtgt, dmask, dlogp, dlse, dent, dwse, wse_bytes, stream));
+    CHECK_RLK(rlk_logp_bwd_ex(&desc, dx, dtgt, dmask, dlse, dent, dg, dgl, dgh, dd2, ld,
+                              RLK_DTYPE_F32, dwse, wse_bytes, stream));
+    CHECK_RLK(rlk_logp_fwd_bwd_ex(&desc, dx, dtgt, dmask, dg, dgl, dgh, dlogp2, dlse2, dent2, dd3,
+                                  ld, RLK_DTYPE_F32, dwsx, wsx_bytes, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(logp, dlogp, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(lse, dlse, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(ent, dent, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(logp2, dlogp2, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(lse2, dlse2, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(ent2, dent2, sizeof(float) * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(d2, dd2, sizeof(float) * n * ld, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(d3, dd3, sizeof(float) * n * ld, hipMemcpyDeviceToHost));
+    same = memcmp(logp, logp2, sizeof(float) * n) == 0 &&
+           memcmp(lse, lse2, sizeof(float) * n) == 0 && memcmp(ent, ent2, sizeof(float) * n) == 0;
+    for (int64_t r = 0; r < n; ++r)
+      same &= memcmp(d2 + r * ld, d3 + r * ld, sizeof(float) * v_pad) == 0;
+    printf("rlk_logp_fwd_bwd_ex bitwise equal to the two extended calls: %s\n",
+           same ? "ok" : "FAIL");
+    failures += !same;
+
+    hipFree(dws1); hipFree(dwse); hipFree(dwsx); hipFree(dgl); hipFree(dgh); hipFree(dent);
+    hipFree(dent2); hipFree(dd2); hipFree(dd3);
+    free(gl); free(gh); free(d2); free(d3); free(ent); free(ent2);
+  }
 
   rlk_logp_desc bad = desc;
   bad.num_vocab_tiles = 0;

@@ -1,6 +1,7 @@
 """The C ABI from plain C: tests/abi_consumer.c links librlk_logp.so and the HIP
 runtime only, and checks shard invariance, the exact gather, the backward's row
-sums and a host error (see its header).  Needs an MI355X."""
+sums, the one-launch calls against the separate ones bit for bit, and a host
+error (see its header).  Needs an MI355X."""
 from __future__ import annotations
 
 import subprocess
