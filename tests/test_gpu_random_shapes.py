@@ -6,7 +6,8 @@ shard counts, mask and ignore rates, logit scale, a few -inf columns):
   * every drawn shard count gives the bits of S = 1;
   * rlk_logp_fwd_bwd gives the bits of the separate calls;
   * rlk_logp_fwd_ex gives the same logp and LSE bits, and its entropy matches
-    the oracle; rlk_logp_bwd_ex matches the oracle's extended backward.
+    the oracle; rlk_logp_bwd_ex matches the oracle's extended backward;
+  * rlk_logp_fwd_bwd_ex gives the bits of rlk_logp_fwd_ex then rlk_logp_bwd_ex.
 The shapes are drawn once from a fixed seed, so the sweep is reproducible.
 """
 from __future__ import annotations
@@ -101,3 +102,12 @@ def test_random_shape(orc, c):
                      raise_on_error=False)
     P.check_bwd_ex(P.dlogits_host(dx), dox, np.zeros(wl.num_tokens, dtype=bool), wl.real_vocab,
                    False, str(c), bits(dx).cpu().numpy().view(np.uint32))
+    # the extended forward and backward in one launch: the bits of the two calls
+    l4, s4, e4, d4 = rlk.forward_backward_ex(inp.logits, inp.targets, inp.mask, inp.grad, gl, gh,
+                                             num_virtual_shards=c["S"], **kw)
+    for a, b, name in ((l4, le, "logp"), (s4, se, "lse"), (e4, ent, "entropy"), (d4, dx, "dX")):
+        na = torch.isnan(a)
+        assert torch.equal(na, torch.isnan(b)), f"one launch extended {name}: NaN pattern"
+        zero = torch.zeros((), dtype=bits(a).dtype, device=DEV)
+        assert torch.equal(torch.where(na, zero, bits(a)), torch.where(na, zero, bits(b))), \
+            f"one launch extended {name}: bits differ"
