@@ -10,7 +10,14 @@
 //                    LSE.
 //   bwd_dlogits      dX = g * (onehot - exp(X - LSE)) on effective-active rows;
 //                    optionally plus the LSE and entropy gradients.
-// plus fwd_bwd_rows, all three in one launch when g is known up front.
+// plus two one-launch forms for when g is known up front, each giving the bits
+// of the three kernels above:
+//   fwd_bwd_rows     one block per row: reads the row twice (partials, then dX).
+//   fwd_bwd_units    blocks of 8 tiles of a row keep their logits on chip, post
+//                    their tile partials to 64-bit slots in the workspace, wait
+//                    (bounded) for the row's other tiles, then write dX: one HBM
+//                    read and one write per element.  With the entropy flag it
+//                    also carries the entropy statistic and its gradients.
 //
 // Sources (web pages, by title and section): PR #289 "[WS2][PR4][Logp] feat:
 // add distributed TP/CP logprob drift report", stacked PR1 commit messages
@@ -21,10 +28,12 @@
 // validation and reproduction guide for Issue #241 PR1-PR5", "4. Cross-Topology
 // Bitwise Check" (outputs identical whatever the tile grouping).
 //
-// Determinism: no atomics; every tile is reduced by the same 16-lane lane
-// mapping (lane l of the group takes the tile's full 16-byte chunks l, l+16,
-// ...) and the same fixed DPP tree whatever launch or shard computes it; the
-// merge runs in ascending tile order.  The file is built with
+// Determinism: no atomic arithmetic on any result (the unit schedule's slots
+// are written by plain 64-bit atomic stores, each by one tile, and its only
+// atomic add counts fallback blocks in a status word); every tile is reduced
+// by the same 16-lane lane mapping (lane l of the group takes the tile's full
+// 16-byte chunks l, l+16, ...) and the same fixed DPP tree whatever launch or
+// shard computes it; the merge runs in ascending tile order.  The file is built with
 // -ffp-contract=off so that only the fmaf calls written here fuse.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
