@@ -106,9 +106,11 @@ def measured_ceilings():
     return out
 
 
-def read_traffic(kernel: str, path: Path = TRAFFIC_FILE, source: Path = KERNEL_SOURCE):
+def read_traffic(kernel: str, workload: str, path: Path = TRAFFIC_FILE,
+                 source: Path = KERNEL_SOURCE):
     """HBM bytes per launch of `kernel` from a committed counter summary, or None
-    when the summary is missing or was taken on a different kernel source."""
+    when the summary is missing, was taken on another workload or on a different
+    kernel source."""
     if not path.exists():
         return None
     vals = {}
@@ -116,7 +118,8 @@ def read_traffic(kernel: str, path: Path = TRAFFIC_FILE, source: Path = KERNEL_S
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_sha(source):
+    if (vals.get("workload") != workload
+            or vals.get("kernel_source_sha256") != kernel_source_sha(source)):
         return None
     key = f"{kernel}_hbm_bytes_per_launch"
     return float(vals[key]) if key in vals else None
@@ -396,7 +399,7 @@ def bench_lmhead(args) -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": read_traffic("lmhead_segments", LMHEAD_TRAFFIC_FILE,
+                     "traffic": read_traffic("lmhead_segments", wl.name, LMHEAD_TRAFFIC_FILE,
                                              LMHEAD_SOURCE),
                      "kernel": "lmhead_segments+lmhead_tiles+stage2_merge"},
         "cpu_baseline": cpu,
@@ -610,7 +613,8 @@ def main() -> int:
                            "fallback_blocks": unit_fallbacks(ws, one_kernel)}}
         roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": None if extended else read_traffic(one_kernel), "kernel": kname}
+                    "traffic": None if extended else read_traffic(one_kernel, wl.name),
+                    "kernel": kname}
     else:
         if extended:  # every row's logits are read again (the LSE and entropy terms reach all)
             nb = dict(nb)
@@ -632,7 +636,7 @@ def main() -> int:
         roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                     "traffic": None if extended else read_traffic(
-                        "bwd_dlogits" if dom == "bwd_dlogits" else "stage1"),
+                        "bwd_dlogits" if dom == "bwd_dlogits" else "stage1", wl.name),
                     "kernel": dom}
 
     # the dominant kernel against this GPU's measured stream ceilings: the time its

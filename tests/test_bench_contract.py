@@ -49,8 +49,19 @@ def test_fp32_dlogits_count_four_bytes():
 def test_committed_traffic_matches_the_current_kernels():
     """The counter summaries under profiles/ were taken on the kernel sources as they
     stand (the bench line reports traffic only while the hashes agree)."""
-    assert bench.read_traffic("bwd_dlogits") is not None
-    assert bench.read_traffic("stage1") is not None
-    assert bench.read_traffic("fwd_bwd_units") is not None
-    assert bench.read_traffic("lmhead_segments", bench.LMHEAD_TRAFFIC_FILE,
+    big = W.LARGE_32K.name
+    assert bench.read_traffic("bwd_dlogits", big) is not None
+    assert bench.read_traffic("stage1", big) is not None
+    assert bench.read_traffic("fwd_bwd_units", big) is not None
+    assert bench.read_traffic("lmhead_segments", bench.LMHEAD_WORKLOAD, bench.LMHEAD_TRAFFIC_FILE,
                               bench.LMHEAD_SOURCE) is not None
+
+
+def test_traffic_is_reported_only_for_the_workload_it_was_taken_on():
+    """The counters were taken on the 32768-row and the 4096-token LM-head workloads;
+    a bench line for any other workload carries no traffic figure."""
+    for wl in (W.MATRIX_B2S16, W.MICROBATCH_1024, W.THROUGHPUT_16K):
+        for k in ("bwd_dlogits", "stage1", "fwd_bwd_units"):
+            assert bench.read_traffic(k, wl.name) is None
+    assert bench.read_traffic("lmhead_segments", W.LARGE_32K.name,
+                              bench.LMHEAD_TRAFFIC_FILE, bench.LMHEAD_SOURCE) is None
