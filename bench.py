@@ -399,7 +399,7 @@ def bench_lmhead(args) -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": read_traffic("lmhead_segments", wl.name, LMHEAD_TRAFFIC_FILE,
+                     "traffic": read_traffic("lmhead_segments", LMHEAD_WORKLOAD, LMHEAD_TRAFFIC_FILE,
                                              LMHEAD_SOURCE),
                      "kernel": "lmhead_segments+lmhead_tiles+stage2_merge"},
         "cpu_baseline": cpu,

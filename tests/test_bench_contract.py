@@ -65,3 +65,29 @@ def test_traffic_is_reported_only_for_the_workload_it_was_taken_on():
             assert bench.read_traffic(k, wl.name) is None
     assert bench.read_traffic("lmhead_segments", W.LARGE_32K.name,
                               bench.LMHEAD_TRAFFIC_FILE, bench.LMHEAD_SOURCE) is None
+
+
+def test_no_undefined_global_names():
+    """Every global name a function of the bench, the input generators, the entry
+    points or the binding reads exists in its module or in builtins (the GPU-only
+    code paths of these files do not run on the CPU)."""
+    import builtins
+    import importlib
+    import symtable
+
+    for name in ("bench", "workloads", "__graft_entry__", "vocab_selected_token_amd"):
+        mod = importlib.import_module(name)
+        src = Path(mod.__file__).read_text()
+        missing = []
+
+        def walk(t):
+            for s in t.get_symbols():
+                n = s.get_name()
+                if (s.is_referenced() and s.is_global() and not hasattr(mod, n)
+                        and not hasattr(builtins, n)):
+                    missing.append((t.get_name(), n))
+            for c in t.get_children():
+                walk(c)
+
+        walk(symtable.symtable(src, mod.__file__, "exec"))
+        assert missing == [], (name, missing)

@@ -324,39 +324,63 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 #pragma unroll
         for (int i = 0; i < 4; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
     } else {
-      // pass 1: per-segment maxima over this lane's rows in [row_lo, row_hi)
+      // Segment 0 is the rows [row_lo, min(row_hi, bnd)), segment 1 the rows
+      // [max(row_lo, bnd), row_hi).  A 16-row tile wholly inside one segment
+      // takes its rows without per-row tests; only a tile that a bound cuts
+      // tests each row.  Rows outside both segments add nothing, exactly as
+      // the per-row form's exp(-inf) = +0 addends do, so the sums keep their
+      // bits; the maxima do not depend on the order.
+      const int32_t end0 = min(row_hi, bnd), beg1 = max(row_lo, bnd);
+      // pass 1: per-segment maxima over this lane's rows
 #pragma unroll
-      for (int vs = 0; vs < kVS; ++vs)
+      for (int vs = 0; vs < kVS; ++vs) {
+        const int32_t r0 = vw0 + vs * 16;
+        if (r0 >= row_lo && r0 + 16 <= end0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t row = vw0 + vs * 16 + row_lane + i;
-          const float z = acc[vs][ts][i];
-          const bool in = row >= row_lo && row < row_hi;
-          if (in && row < bnd) m0 = maxnan(m0, z);
-          if (in && row >= bnd) m1 = maxnan(m1, z);
+          for (int i = 0; i < 4; ++i) m0 = maxnan(m0, acc[vs][ts][i]);
+        } else if (r0 >= beg1 && r0 + 16 <= row_hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m1 = maxnan(m1, acc[vs][ts][i]);
+        } else if (r0 + 16 > row_lo && r0 < row_hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t row = r0 + row_lane + i;
+            const float z = acc[vs][ts][i];
+            const bool in = row >= row_lo && row < row_hi;
+            if (in && row < bnd) m0 = maxnan(m0, z);
+            if (in && row >= bnd) m1 = maxnan(m1, z);
+          }
         }
+      }
       m0 = maxnan(m0, __shfl_xor(m0, 16));
       m0 = maxnan(m0, __shfl_xor(m0, 32));
       m1 = maxnan(m1, __shfl_xor(m1, 16));
       m1 = maxnan(m1, __shfl_xor(m1, 32));
-      // pass 2: sums of exp(z - max) relative to the token's maxima.  The two
-      // thresholds go through an empty asm so the compiler recomputes the row
-      // tests here instead of keeping 128 masks alive from pass 1.
-      int32_t lo = row_lo, rv = row_hi, bd = bnd;
-      asm volatile("" : "+s"(lo), "+s"(rv), "+s"(bd));
+      // pass 2: sums of exp(z - max) relative to the token's maxima, in the
+      // same row order as the one-segment form
       const float b0 = (m0 == kNegInf) ? 0.0f : m0;
       const float b1 = (m1 == kNegInf) ? 0.0f : m1;
 #pragma unroll
-      for (int vs = 0; vs < kVS; ++vs)
+      for (int vs = 0; vs < kVS; ++vs) {
+        const int32_t r0 = vw0 + vs * 16;
+        if (r0 >= row_lo && r0 + 16 <= end0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t row = vw0 + vs * 16 + row_lane + i;
-          const float z = (row >= lo && row < rv) ? acc[vs][ts][i] : kNegInf;
-          const bool hi = row >= bd;
-          const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
-          s0 += hi ? 0.0f : e;
-          s1 += hi ? e : 0.0f;
+          for (int i = 0; i < 4; ++i) s0 += exp2_hw((acc[vs][ts][i] - b0) * kLog2e);
+        } else if (r0 >= beg1 && r0 + 16 <= row_hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s1 += exp2_hw((acc[vs][ts][i] - b1) * kLog2e);
+        } else if (r0 + 16 > row_lo && r0 < row_hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t row = r0 + row_lane + i;
+            const float z = (row >= row_lo && row < row_hi) ? acc[vs][ts][i] : kNegInf;
+            const bool hi = row >= bnd;
+            const float e = exp2_hw((z - (hi ? b1 : b0)) * kLog2e);
+            s0 += hi ? 0.0f : e;
+            s1 += hi ? e : 0.0f;
+          }
         }
+      }
     }
     // the four lanes of the token: pairs over 16 lanes, then over 32; each
     // addition has the same two addends in both lanes, so all four agree
