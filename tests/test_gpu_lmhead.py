@@ -183,11 +183,19 @@ SHARD_SWEEP = draw_shard_cases(int(os.environ.get("RLK_LMHEAD_SHARD_SWEEP", "12"
 @pytest.mark.parametrize("c", SHARD_SWEEP,
                          ids=lambda c: "{i}_n{n}_k{k}_v{v_real}_p{v_pad}_T{tiles}".format(**c))
 def test_fused_virtual_shards_sweep(c):
-    """Every drawn shard count gives the bits of S = 1: logp, LSE and every partial."""
+    """Every drawn shard count gives the bits of S = 1: logp, LSE and every partial;
+    and S = 1 matches the oracle (its blocks are cut by tile bounds and the end of
+    the real vocabulary wherever the drawn shape puts them)."""
     print(f"case {c}", flush=True)
     n, t = c["n"], c["tiles"]
     h, w, tgt, mask = make_case(n, c["k"], c["v_real"], c["v_pad"], seed=9000 + c["i"])
     ref = run(h, w, tgt, mask, c["v_real"], c["v_pad"], t)
+    o = oracle.get()
+    z = o.lmhead_logits(bf16_bits(h), bf16_bits(w), real_vocab=c["v_real"])
+    t_h, m_h = tgt.cpu().numpy(), mask.cpu().numpy()
+    lo, so, _, _ = o.fwd(z, t_h, m_h, real_vocab=c["v_real"])
+    P.check_fwd(ref[0].cpu().numpy(), ref[1].cpu().numpy(), lo, so,
+                P.effective_active(t_h, m_h), str(c))
     ref_bits = (ref[0].view(torch.int32).cpu(), ref[1].view(torch.int32).cpu()) + \
         partials(ref[2], n, t)
     for s in c["shards"]:
