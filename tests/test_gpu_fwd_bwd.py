@@ -203,7 +203,7 @@ def assert_same_bits_nan(a3, b3, what):
                          ids=lambda c: f"n{c['n']}_v{c['real']}_p{c['pad']}_T{c['T']}")
 def test_unit_schedule_matches_row_schedule(case):
     """Where the geometry fits, rlk_logp_fwd_bwd with its full workspace runs the
-    unit schedule (blocks of 4 tiles that exchange partials); with only the
+    unit schedule (blocks of 8 tiles that exchange partials); with only the
     status words it runs one block per row.  Both give the bits of the separate
     calls, on rows with NaN, +inf and no finite logit too."""
     print(f"case {case}", flush=True)
