@@ -123,12 +123,19 @@ def _stream(stream) -> int:
 def make_desc(num_tokens: int, real_vocab: int, padded_vocab: int, ld_logits: int,
               num_vocab_tiles: int = 64, num_virtual_shards: int = 1, ignore_index: int = -100,
               validate: bool = False) -> rlk_logp_desc:
+    """The rlk_logp_desc of a call: ld_logits is the row stride of the logits in
+    elements; validate sets RLK_FLAG_VALIDATE."""
     return rlk_logp_desc(num_tokens, real_vocab, padded_vocab, ld_logits, num_vocab_tiles,
                          num_virtual_shards, ignore_index,
                          RLK_FLAG_VALIDATE if validate else 0)
 
 
 # -- the C entry points --------------------------------------------------------
+# Each function below calls the C function of the same name (include/rlk_logp.h)
+# with the same arguments in the same order: tensors go as their data pointers
+# (None as NULL), a workspace tensor also gives its size in bytes, `stream`
+# defaults to torch's current stream, and a status other than RLK_OK raises
+# RlkError with the library's detail text.
 def rlk_logp_workspace_bytes(desc: rlk_logp_desc) -> int:
     return int(_lib.rlk_logp_workspace_bytes(ctypes.byref(desc)))
 
@@ -313,6 +320,8 @@ def _u8_mask(mask):
 
 
 def workspace_for(desc: rlk_logp_desc, device) -> torch.Tensor:
+    """A fresh workspace of rlk_logp_workspace_bytes(desc) bytes for rlk_logp_fwd
+    (its contents on entry do not matter)."""
     n = rlk_logp_workspace_bytes(desc)
     if n == 0:
         raise ValueError(f"invalid rlk_logp_desc: {rlk_last_error_detail()}")
