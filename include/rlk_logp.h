@@ -334,7 +334,8 @@ rlk_status rlk_logp_fwd_bwd_ex(const rlk_logp_desc* desc, const void* logits,
  *   hidden      (device) bf16 [num_tokens, hidden_dim], row-major, 16-byte aligned.
  *   weight      (device) bf16 [padded_vocab, hidden_dim], row-major, 16-byte
  *               aligned; rows >= real_vocab are never read.
- *   hidden_dim  a positive multiple of 64.
+ *   hidden_dim  a positive multiple of 64, at most 2^21 (RLK_ERR_BAD_SHAPE
+ *               otherwise).
  *   targets, active_mask, logp, lse   as for rlk_logp_fwd.
  *   workspace   >= rlk_logp_fused_lmhead_workspace_bytes(desc), 256-byte
  *               aligned.  Its status words and per-tile partials sit where

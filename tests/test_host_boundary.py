@@ -227,6 +227,7 @@ def test_fused_lmhead_host_validation():
               num_virtual_shards=0), 64, rlk.RLK_ERR_BAD_TILING),
         (ok, 96, rlk.RLK_ERR_BAD_SHAPE),  # hidden_dim not a multiple of 64
         (ok, 0, rlk.RLK_ERR_BAD_SHAPE),
+        (ok, (1 << 21) + 64, rlk.RLK_ERR_BAD_SHAPE),  # above 2^21
     ]
     for d, k, code in cases:
         with pytest.raises(rlk.RlkError) as ei:

@@ -656,9 +656,9 @@ rlk_status rlk_logp_fused_lmhead(const rlk_logp_desc* desc, const void* hidden,
   rlk_status st = check_fused_desc(desc);
   if (st != RLK_OK) return st;
   if (hidden_dim < rlk::kLmheadSlabK || hidden_dim % rlk::kLmheadSlabK != 0 ||
-      hidden_dim > kI32Max)
-    return fail(RLK_ERR_BAD_SHAPE, "hidden_dim=%lld must be a positive multiple of %d",
-                (long long)hidden_dim, rlk::kLmheadSlabK);
+      hidden_dim > rlk::kLmheadMaxHidden)
+    return fail(RLK_ERR_BAD_SHAPE, "hidden_dim=%lld must be a positive multiple of %d, at most %lld",
+                (long long)hidden_dim, rlk::kLmheadSlabK, (long long)rlk::kLmheadMaxHidden);
   const int64_t n = desc->num_tokens;
   if (n == 0) return ok();
   if (!hidden || !weight || !targets || !logp || !lse)

@@ -110,6 +110,9 @@ int32_t fwd_bwd_spin_limit();
 // least this wide, so a block holds at most one tile bound).
 constexpr int32_t kLmheadBlockVocab = 256;
 constexpr int32_t kLmheadSlabK = 64;  // hidden_dim must be a multiple of this
+// and at most this: a block's 256 rows of one operand then span under 2^31
+// bytes, the range of the buffer resource its loads go through
+constexpr int64_t kLmheadMaxHidden = int64_t{1} << 21;
 
 struct LmheadArgs {
   const void* hidden;  // bf16 [num_tokens, hidden_dim]

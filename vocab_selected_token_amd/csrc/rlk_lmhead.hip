@@ -33,8 +33,11 @@
 // one wave's MFMAs run while the other waits on memory.
 //
 // K advances in slabs of 64 (two k-steps) through two LDS stages filled by
-// direct global-to-LDS loads (global_load_lds_dwordx4: lane i of an
-// instruction writes bytes [16i, 16i + 16) after the wave's LDS base).  LDS
+// direct global-to-LDS loads (buffer_load_dwordx4 ... lds: lane i of an
+// instruction writes bytes [16i, 16i + 16) after the wave's LDS base; the
+// address is a buffer resource per operand based at the block's first row, a
+// fixed 32-bit byte offset per lane and the slab's offset in a scalar
+// register, so a load needs no address arithmetic).  LDS
 // rows are 128 bytes with the 16-byte chunks XOR-swizzled by row -- chunk c of
 // row r sits at position c ^ ((r >> 1) & 7) -- so that fragment reads of
 // consecutive rows at one chunk spread over the bank groups; each load lane
@@ -82,6 +85,10 @@ static_assert(kBV == kLmheadBlockVocab, "block width shared with the boundary");
 static_assert(kBV == kBT, "the load mapping assumes square blocks");
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Word 3 of a raw (untyped) buffer resource on gfx9: 32-bit data format, no
+// swizzle, no thread-id addressing.
+constexpr int kBufferWord3 = 0x00020000;
 
 // LDS position (in 16-byte units) of chunk c of row r inside one operand stage.
 __device__ __forceinline__ int swizzled(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -161,17 +168,26 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
 
   // Direct loads: wave w moves rows [32w, 32w + 32) of both operands, 8 rows per
   // instruction; lane i of instruction j fetches row 32w + 8j + i/8 at the chunk
-  // that belongs at LDS position i%8.  Offsets are in 16-byte chunks from the
-  // operand base (the boundary checks that both operands hold fewer than 2^31
-  // chunks); rows of W outside [row_lo, row_hi) -- padding, other shards --
-  // and rows past the last token are never read.
-  int32_t woff[kLoads], hoff[kLoads];
+  // that belongs at LDS position i%8.  Rows of W outside [row_lo, row_hi) --
+  // padding, other shards -- and rows past the last token are never read: the
+  // row is clamped, and each operand's buffer resource covers only the block's
+  // rows (at most 256 rows of 2 * hidden_dim bytes, under 2^31 bytes by the
+  // boundary's limit on hidden_dim), starting at its first row read.
+  const int32_t w_first = max(v0, row_lo);
+  const int64_t row_bytes = (int64_t)ldc * 16;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w + (int64_t)w_first * ldc), 0,
+      (int)((int64_t)(min(v0 + kBV, row_hi) - w_first) * row_bytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(h + (int64_t)t0 * ldc), 0,
+      (int)((int64_t)(min(t0 + kBT, num_tokens) - t0) * row_bytes), kBufferWord3);
+  uint32_t woff[kLoads], hoff[kLoads];  // byte offsets from the resources' bases
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const int row = wave * kRowsPerWave + j * kRowsPerLoad + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    woff[j] = min(max(v0 + row, row_lo), row_hi - 1) * ldc + c;
-    hoff[j] = min(t0 + row, num_tokens - 1) * ldc + c;
+    woff[j] = (uint32_t)((min(max(v0 + row, row_lo), row_hi - 1) - w_first) * row_bytes + c * 16);
+    hoff[j] = (uint32_t)((min(t0 + row, num_tokens - 1) - t0) * row_bytes + c * 16);
   }
 
   constexpr int kVS = 8;  // 16-row vocabulary tiles per wave
@@ -188,16 +204,16 @@ __global__ __launch_bounds__(kThreads) void lmhead_segments(
   // slab `slab` into LDS stage `stage` (A = W rows at the stage base, B = hidden rows after)
   auto issue = [&](int slab, int stage) __attribute__((always_inline)) {
     char* base = smem + stage * 2 * kSlabBytes + (wave * kRowsPerWave) * kRowBytes;
+    const uint32_t soff = (uint32_t)slab * kRowBytes;  // the slab's bytes in a row
     // all W rows, then all hidden rows (about 0.6% faster than alternating)
 #pragma unroll
     for (int j = 0; j < kLoads; ++j)
-      __builtin_amdgcn_global_load_lds(w + woff[j] + slab * (kBK / 8),
-                                       (lds_ptr)(base + j * kRowsPerLoad * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(base + j * kRowsPerLoad * kRowBytes),
+                                               16, woff[j], soff, 0, 0);
 #pragma unroll
     for (int j = 0; j < kLoads; ++j)
-      __builtin_amdgcn_global_load_lds(h + hoff[j] + slab * (kBK / 8),
-                                       (lds_ptr)(base + kSlabBytes + j * kRowsPerLoad * kRowBytes),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          hrs, (lds_ptr)(base + kSlabBytes + j * kRowsPerLoad * kRowBytes), 16, hoff[j], soff, 0, 0);
   };
   // fragment reads of k-step ks: lane l takes row l%16 of each 16-row tile at
   // chunk 4ks + l/16 (k in [32ks + 8(l/16), +8))
